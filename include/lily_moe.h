@@ -1,0 +1,162 @@
+/*
+ * lily_moe.h: C ABI of the int4 grouped-GEMM MoE layer for MI355X (gfx950).
+ *
+ * The layer is the prefill Mixture-of-Experts block described in the Lily
+ * articles (news.ainew.jp, "Perplexity, Apple Silicon向け推論エンジン「Lily」を
+ * オープンソース化"):
+ *   - the router picks k of E experts per token and a shared expert also
+ *     processes every token (section on the three workload shapes);
+ *   - the weights are groupwise-affine 4-bit: 64 weights share one bf16
+ *     scale and one bf16 bias; they are rebuilt as bf16 tile by tile inside
+ *     the grouped GEMM, kept on chip, and the products accumulate in FP32
+ *     (section "Prefill");
+ *   - the routing histogram, prefix scan, scatter and block map stay on the
+ *     GPU, in one stream, with no host synchronisation inside the layer
+ *     (section "Prefill").
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless stated. The caller allocates and
+ *     owns every buffer and keeps it alive until the stream work completes.
+ *     The library allocates no device memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue work and return; none synchronises the host.
+ *   - Return value 0 (LILY_OK) or a negative LILY_ERR_* code. Argument checks
+ *     are done on the host before anything is enqueued; on an error nothing is
+ *     enqueued and lily_last_error() describes it. Faults inside a kernel
+ *     surface at the caller's next synchronisation. No C++ exception crosses
+ *     this interface.
+ *   - The calls are re-entrant for distinct buffers and streams.
+ *   - Device pointers must be 16-byte aligned.
+ *
+ * Readings of points the pages leave open (the same readings the CPU oracle
+ * takes): groups of 64 run along K, the input dimension of an [N, K]
+ * (out x in) matrix, and byte i of a row packs element 2i in its low nibble;
+ * w = scale*q + bias rounded to bf16; ties in top-k go to the lower expert
+ * index (-0.0 ties +0.0); routing weights are a softmax over the k selected
+ * logits; each expert is a SwiGLU FFN h = bf16(silu(x Wg^T) * (x Wu^T)),
+ * y = h Wd^T in fp32; the shared expert has weight 1; the output is
+ * bf16(y_shared + sum_j w_j y_j) summed in slot order.
+ */
+#ifndef LILY_MOE_H
+#define LILY_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LILY_OK 0
+#define LILY_ERR_INVALID_ARG (-1) /* null pointer, bad size, misaligned pointer */
+#define LILY_ERR_UNSUPPORTED (-2) /* a shape or tile the kernels do not cover */
+#define LILY_ERR_WORKSPACE (-3)   /* workspace smaller than required */
+#define LILY_ERR_HIP (-4)         /* a HIP launch error; text from hipGetErrorString */
+
+/* Layer sizes. T tokens, hidden size H, expert FFN size F, E routed experts,
+   topk experts per token, group = 64 (the only supported group), tile_m =
+   rows per block of the block map (32, 64 or 128 for lily_moe_forward; any
+   value >= 1 for lily_moe_route). H and F must be multiples of 64;
+   1 <= topk <= E <= 512; T >= 1. */
+typedef struct {
+    int32_t T, H, F, E, topk, group, tile_m;
+} lily_moe_dims;
+
+/* One groupwise-affine int4 matrix per expert, stacked over n experts
+   (n = E for routed, 1 for the shared expert), for a matrix of N rows
+   (outputs) and K columns (inputs):
+     q:     uint8 [n, N, K/2]; byte i of a row = element 2i (low nibble)
+            and element 2i+1 (high nibble), values 0..15;
+     scale: bf16 bits [n, N, K/64];
+     bias:  bf16 bits [n, N, K/64];
+   weight (e, row, col) = bf16(scale[e,row,col/64] * q + bias[e,row,col/64]). */
+typedef struct {
+    const uint8_t* q;
+    const uint16_t* scale;
+    const uint16_t* bias;
+} lily_w4;
+
+/* gate, up: N = F, K = H.  down: N = H, K = F. */
+typedef struct {
+    lily_w4 gate, up, down;          /* routed experts, n = E */
+    lily_w4 sh_gate, sh_up, sh_down; /* shared expert, n = 1 */
+} lily_moe_weights;
+
+/* Outputs of lily_moe_route (inputs of lily_moe_forward). P = T * topk.
+   topk_ids  int32 [T, topk]  chosen experts, descending logit;
+   topk_w    fp32  [T, topk]  softmax of the chosen logits;
+   counts    int32 [E]        rows per expert (histogram);
+   offsets   int32 [E + 1]    exclusive scan of counts, offsets[E] = P;
+   sorted_pairs int32 [P]     row r of the expert-ordered layout holds pair
+                              p = t * topk + j; rows of one expert are in
+                              ascending p (stable);
+   pair_rows int32 [P]        inverse: pair_rows[sorted_pairs[r]] = r;
+   block_expert, block_row0 int32 [lily_moe_max_blocks(dims)]
+                              block b covers rows block_row0[b] ..
+                              min(block_row0[b] + tile_m, offsets[e+1]) - 1 of
+                              expert e = block_expert[b]; experts ascending;
+                              entries at and past num_blocks are unspecified;
+   num_blocks int32 [1]       number of valid blocks (stays on the device). */
+typedef struct {
+    int32_t* topk_ids;
+    float* topk_w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_pairs;
+    int32_t* pair_rows;
+    int32_t* block_expert;
+    int32_t* block_row0;
+    int32_t* num_blocks;
+} lily_moe_routing;
+
+/* Host, pure. Capacity of the block map: ceil(P / tile_m) + min(E, P).
+   Returns a negative LILY_ERR_* code for invalid dims. */
+int32_t lily_moe_max_blocks(const lily_moe_dims* dims);
+
+/* Host, pure. Bytes of device workspace lily_moe_forward needs for dims
+   (0 for invalid dims). The workspace holds the SwiGLU intermediate h (bf16)
+   and the per-row expert outputs y (fp32) for the P routed rows and the T
+   shared rows. */
+size_t lily_moe_workspace_bytes(const lily_moe_dims* dims);
+
+/* Routing of one MoE layer: top-k and softmax per token, histogram,
+   exclusive scan, stable scatter and block map, all enqueued on `stream`
+   with no host synchronisation.
+   logits: fp32 [T, E] router scores. Deterministic and bit-exact for
+   finite logits; non-finite logits give unspecified (but in-bounds) output.
+   Errors: LILY_ERR_INVALID_ARG (null pointer, bad dims, misalignment),
+   LILY_ERR_UNSUPPORTED (E > 512 or topk > 64), LILY_ERR_HIP. */
+int lily_moe_route(const lily_moe_dims* dims, const float* logits,
+                   const lily_moe_routing* routing, void* stream);
+
+/* Expert computation of one MoE layer from a routing produced by
+   lily_moe_route with the same dims: grouped gate/up GEMM with the int4 ->
+   bf16 dequantisation fused into the tile loads, SwiGLU, grouped down GEMM,
+   the shared expert, and the weighted gather-combine.
+   x: bf16 bits [T, H]; out: bf16 bits [T, H]; workspace: at least
+   lily_moe_workspace_bytes(dims) bytes of device memory (contents on entry
+   are ignored). The routing is trusted (ids in range, block map as produced
+   by lily_moe_route). Run-to-run deterministic: no floating-point atomics.
+   Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (tile_m not 32/64/128,
+   H or F not a multiple of 128), LILY_ERR_WORKSPACE, LILY_ERR_HIP. */
+int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                     const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Residual stream between stacked MoE layers (the pages describe a stack of
+   layers but not this glue; the reading is a pre-norm residual with a
+   unit-gain RMSNorm): r += out (fp32), then
+   x_next = bf16(r / sqrt(mean(r^2) + eps)) per token.
+   r: fp32 [T, H] in/out; out: bf16 bits [T, H], or NULL to only normalise;
+   x_next: bf16 bits [T, H]. Errors: LILY_ERR_INVALID_ARG, LILY_ERR_HIP. */
+int lily_residual_norm(int32_t T, int32_t H, float* r, const uint16_t* out,
+                       uint16_t* x_next, float eps, void* stream);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* lily_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LILY_MOE_H */

@@ -1,0 +1,234 @@
+"""Python binding of ``liblily_moe.so``: the int4 grouped-GEMM MoE layer on MI355X.
+
+The functions below carry the C ABI's names (``include/lily_moe.h``) and do
+argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch provides device memory and streams. There is no fallback:
+if the library has not been built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblily_moe.so")
+
+LILY_OK = 0
+LILY_ERR_INVALID_ARG = -1
+LILY_ERR_UNSUPPORTED = -2
+LILY_ERR_WORKSPACE = -3
+LILY_ERR_HIP = -4
+
+EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_moe_route",
+           "lily_moe_forward", "lily_residual_norm", "lily_last_error")
+
+
+class LilyMoeDims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("F", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32)]
+
+
+class LilyW4(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+class LilyMoeWeights(ctypes.Structure):
+    _fields_ = [(n, LilyW4) for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")]
+
+
+ROUTING_FIELDS = ("topk_ids", "topk_w", "counts", "offsets", "sorted_pairs", "pair_rows",
+                  "block_expert", "block_row0", "num_blocks")
+
+
+class LilyMoeRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ROUTING_FIELDS]
+
+
+class LilyError(RuntimeError):
+    def __init__(self, code: int, text: str):
+        super().__init__(f"lily error {code}: {text}")
+        self.code = code
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library. Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -c 'import __graft_entry__ as g;"
+                           f" g.build()'` (or int4_grouped_gemm_amd/build.py)")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER
+    lib.lily_moe_max_blocks.restype = ctypes.c_int32
+    lib.lily_moe_max_blocks.argtypes = [P(LilyMoeDims)]
+    lib.lily_moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.lily_moe_workspace_bytes.argtypes = [P(LilyMoeDims)]
+    lib.lily_moe_route.restype = ctypes.c_int
+    lib.lily_moe_route.argtypes = [P(LilyMoeDims), ctypes.c_void_p, P(LilyMoeRouting),
+                                   ctypes.c_void_p]
+    lib.lily_moe_forward.restype = ctypes.c_int
+    lib.lily_moe_forward.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
+                                     P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
+    lib.lily_residual_norm.restype = ctypes.c_int
+    lib.lily_residual_norm.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                       ctypes.c_void_p]
+    lib.lily_last_error.restype = ctypes.c_char_p
+    lib.lily_last_error.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- marshalling
+
+def dims(T: int, H: int, F: int, E: int, topk: int, tile_m: int = 64,
+         group: int = 64) -> LilyMoeDims:
+    return LilyMoeDims(T, H, F, E, topk, group, tile_m)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, lib: ctypes.CDLL) -> None:
+    if rc != LILY_OK:
+        raise LilyError(rc, lib.lily_last_error().decode())
+
+
+@dataclasses.dataclass
+class W4:
+    """One stacked int4 matrix set on the device (uint8 q, int16 bf16 bits)."""
+
+    q: torch.Tensor
+    scale: torch.Tensor
+    bias: torch.Tensor
+
+    def c(self) -> LilyW4:
+        return LilyW4(_ptr(self.q), _ptr(self.scale), _ptr(self.bias))
+
+
+@dataclasses.dataclass
+class Weights:
+    gate: W4
+    up: W4
+    down: W4
+    sh_gate: W4
+    sh_up: W4
+    sh_down: W4
+
+    def c(self) -> LilyMoeWeights:
+        return LilyMoeWeights(*(getattr(self, n).c() for n in
+                                ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")))
+
+
+@dataclasses.dataclass
+class Routing:
+    topk_ids: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    sorted_pairs: torch.Tensor
+    pair_rows: torch.Tensor
+    block_expert: torch.Tensor
+    block_row0: torch.Tensor
+    num_blocks: torch.Tensor
+
+    def c(self) -> LilyMoeRouting:
+        return LilyMoeRouting(*(_ptr(getattr(self, n)) for n in ROUTING_FIELDS))
+
+
+def lily_moe_max_blocks(d: LilyMoeDims) -> int:
+    lib = load()
+    n = lib.lily_moe_max_blocks(ctypes.byref(d))
+    _check(min(n, 0), lib)
+    return n
+
+
+def lily_moe_workspace_bytes(d: LilyMoeDims) -> int:
+    lib = load()
+    n = lib.lily_moe_workspace_bytes(ctypes.byref(d))
+    if n == 0:
+        raise LilyError(LILY_ERR_INVALID_ARG, lib.lily_last_error().decode())
+    return n
+
+
+def lily_moe_route(d: LilyMoeDims, logits, routing: Routing, stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_route(ctypes.byref(d), _ptr(logits), ctypes.byref(routing.c()),
+                            _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_forward(d: LilyMoeDims, weights: Weights, x, routing: Routing, out, workspace,
+                     workspace_bytes: Optional[int] = None, stream=None) -> None:
+    lib = load()
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = lib.lily_moe_forward(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(x),
+                              ctypes.byref(routing.c()), _ptr(out), _ptr(workspace),
+                              workspace_bytes, _stream(stream))
+    _check(rc, lib)
+
+
+def lily_residual_norm(T: int, H: int, r, out, x_next, eps: float = 1e-6, stream=None) -> None:
+    lib = load()
+    rc = lib.lily_residual_norm(T, H, _ptr(r), _ptr(out), _ptr(x_next), eps, _stream(stream))
+    _check(rc, lib)
+
+
+def lily_last_error() -> str:
+    return load().lily_last_error().decode()
+
+
+# ----------------------------------------------------------------- allocation
+
+def alloc_routing(d: LilyMoeDims, device="cuda") -> Routing:
+    """Device buffers for one layer's routing (the library allocates nothing)."""
+    T, E, k = d.T, d.E, d.topk
+    P = T * k
+    mb = lily_moe_max_blocks(d)
+    i32 = dict(dtype=torch.int32, device=device)
+    return Routing(topk_ids=torch.empty((T, k), **i32),
+                   topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
+                   counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                   sorted_pairs=torch.empty(P, **i32), pair_rows=torch.empty(P, **i32),
+                   block_expert=torch.empty(mb, **i32), block_row0=torch.empty(mb, **i32),
+                   num_blocks=torch.empty(1, **i32))
+
+
+def alloc_workspace(d: LilyMoeDims, device="cuda") -> torch.Tensor:
+    return torch.empty(lily_moe_workspace_bytes(d), dtype=torch.uint8, device=device)
+
+
+def weights_from_host(lw, device="cuda") -> Weights:
+    """Upload a ``synth.LayerWeights`` (numpy, canonical layout) to the device."""
+    def up(w) -> W4:
+        return W4(torch.from_numpy(w.q).to(device),
+                  torch.from_numpy(w.scale.view("int16")).to(device),
+                  torch.from_numpy(w.bias.view("int16")).to(device))
+    return Weights(up(lw.gate), up(lw.up), up(lw.down), up(lw.sh_gate), up(lw.sh_up),
+                   up(lw.sh_down))

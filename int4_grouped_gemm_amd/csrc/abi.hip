@@ -1,0 +1,164 @@
+// C ABI of the MoE layer: argument checks on the host, then launches.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.hpp"
+
+namespace lily {
+
+static thread_local char g_last_error[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int check_launch(const char* what) {
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return set_error(LILY_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+    return LILY_OK;
+}
+
+int launch_route(const lily_moe_dims& d, const float* logits, const lily_moe_routing& r,
+                 hipStream_t stream);
+int launch_forward(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+                   const lily_moe_routing& r, uint16_t* out, void* ws, int max_blocks,
+                   hipStream_t stream);
+size_t forward_workspace_bytes(const lily_moe_dims& d);
+int launch_residual_norm(int T, int H, float* r, const uint16_t* out, uint16_t* x_next,
+                         float eps, hipStream_t stream);
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                                   \
+    do {                                                                                 \
+        if (!(p)) return set_error(LILY_ERR_INVALID_ARG, "%s is NULL", #p);              \
+        if (!aligned16(p)) return set_error(LILY_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+static int check_dims(const lily_moe_dims* d) {
+    if (!d) return set_error(LILY_ERR_INVALID_ARG, "dims is NULL");
+    if (d->T < 1) return set_error(LILY_ERR_INVALID_ARG, "T = %d < 1", d->T);
+    if (d->E < 1) return set_error(LILY_ERR_INVALID_ARG, "E = %d < 1", d->E);
+    if (d->topk < 1 || d->topk > d->E)
+        return set_error(LILY_ERR_INVALID_ARG, "topk = %d not in [1, E = %d]", d->topk, d->E);
+    if (d->group != kGroup)
+        return set_error(LILY_ERR_INVALID_ARG, "group = %d; only 64 is supported", d->group);
+    if (d->H < kGroup || d->H % kGroup)
+        return set_error(LILY_ERR_INVALID_ARG, "H = %d is not a positive multiple of 64", d->H);
+    if (d->F < kGroup || d->F % kGroup)
+        return set_error(LILY_ERR_INVALID_ARG, "F = %d is not a positive multiple of 64", d->F);
+    if (d->tile_m < 1) return set_error(LILY_ERR_INVALID_ARG, "tile_m = %d < 1", d->tile_m);
+    if ((int64_t)d->T * d->topk + d->T > (int64_t)1 << 30)
+        return set_error(LILY_ERR_UNSUPPORTED, "T * (topk + 1) too large");
+    if (d->E > kMaxExperts)
+        return set_error(LILY_ERR_UNSUPPORTED, "E = %d > %d", d->E, kMaxExperts);
+    if (d->topk > kMaxTopk)
+        return set_error(LILY_ERR_UNSUPPORTED, "topk = %d > %d", d->topk, kMaxTopk);
+    return LILY_OK;
+}
+
+static int32_t max_blocks_of(const lily_moe_dims& d) {
+    const int64_t P = (int64_t)d.T * d.topk;
+    const int64_t nb = (P + d.tile_m - 1) / d.tile_m + (P < d.E ? P : d.E);
+    return (int32_t)nb;
+}
+
+static int check_routing(const lily_moe_routing* r) {
+    if (!r) return set_error(LILY_ERR_INVALID_ARG, "routing is NULL");
+    REQUIRE_PTR(r->topk_ids);
+    REQUIRE_PTR(r->topk_w);
+    REQUIRE_PTR(r->counts);
+    REQUIRE_PTR(r->offsets);
+    REQUIRE_PTR(r->sorted_pairs);
+    REQUIRE_PTR(r->pair_rows);
+    REQUIRE_PTR(r->block_expert);
+    REQUIRE_PTR(r->block_row0);
+    REQUIRE_PTR(r->num_blocks);
+    return LILY_OK;
+}
+
+static int check_w4(const lily_w4& w, const char* name) {
+    if (!w.q || !w.scale || !w.bias)
+        return set_error(LILY_ERR_INVALID_ARG, "weights.%s has a NULL pointer", name);
+    if (!aligned16(w.q) || !aligned16(w.scale) || !aligned16(w.bias))
+        return set_error(LILY_ERR_INVALID_ARG, "weights.%s is not 16-byte aligned", name);
+    return LILY_OK;
+}
+
+}  // namespace lily
+
+using namespace lily;
+
+extern "C" {
+
+int32_t lily_moe_max_blocks(const lily_moe_dims* dims) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    return max_blocks_of(*dims);
+}
+
+size_t lily_moe_workspace_bytes(const lily_moe_dims* dims) {
+    if (check_dims(dims)) return 0;
+    return forward_workspace_bytes(*dims);
+}
+
+int lily_moe_route(const lily_moe_dims* dims, const float* logits,
+                   const lily_moe_routing* routing, void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    REQUIRE_PTR(logits);
+    rc = check_routing(routing);
+    if (rc) return rc;
+    return launch_route(*dims, logits, *routing, reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                     const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!weights) return set_error(LILY_ERR_INVALID_ARG, "weights is NULL");
+    if ((rc = check_w4(weights->gate, "gate")) || (rc = check_w4(weights->up, "up")) ||
+        (rc = check_w4(weights->down, "down")) || (rc = check_w4(weights->sh_gate, "sh_gate")) ||
+        (rc = check_w4(weights->sh_up, "sh_up")) || (rc = check_w4(weights->sh_down, "sh_down")))
+        return rc;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(out);
+    rc = check_routing(routing);
+    if (rc) return rc;
+    if (dims->tile_m != 32 && dims->tile_m != 64 && dims->tile_m != 128)
+        return set_error(LILY_ERR_UNSUPPORTED, "tile_m = %d; forward supports 32, 64, 128",
+                         dims->tile_m);
+    if (dims->H % 128 || dims->F % 64)
+        return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 128", dims->H);
+    const size_t need = forward_workspace_bytes(*dims);
+    if (!workspace) return set_error(LILY_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned16(workspace))
+        return set_error(LILY_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+        return set_error(LILY_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+                         workspace_bytes, need);
+    return launch_forward(*dims, *weights, x, *routing, out, workspace, max_blocks_of(*dims),
+                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_residual_norm(int32_t T, int32_t H, float* r, const uint16_t* out, uint16_t* x_next,
+                       float eps, void* stream) {
+    if (T < 1 || H < 4 || H % 4)
+        return set_error(LILY_ERR_INVALID_ARG, "T = %d, H = %d (need T >= 1, H %% 4 == 0)", T, H);
+    if (!(eps >= 0.0f)) return set_error(LILY_ERR_INVALID_ARG, "eps must be >= 0");
+    REQUIRE_PTR(r);
+    REQUIRE_PTR(x_next);
+    if (out && !aligned16(out))
+        return set_error(LILY_ERR_INVALID_ARG, "out is not 16-byte aligned");
+    return launch_residual_norm(T, H, r, out, x_next, eps, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char* lily_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal helpers shared by the HIP sources of the MoE layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lily_moe.h"
+
+namespace lily {
+
+constexpr int kWave = 64;      // CDNA wavefront width
+constexpr int kGroup = 64;     // weights per (scale, bias) group
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopk = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// Two floats -> packed bf16x2 bits, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
+}
+
+// Host-side launch bookkeeping shared by the sources.
+struct LaunchError {
+    int code;
+    const char* what;
+};
+
+// Records the thread's last error text; returns code.
+int set_error(int code, const char* fmt, ...);
+int check_launch(const char* what);
+
+}  // namespace lily

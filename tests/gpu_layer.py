@@ -1,0 +1,70 @@
+"""Helpers for the GPU tests: upload seeded inputs and run the layer through
+the C ABI (``int4_grouped_gemm_amd``), and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import int4_grouped_gemm_amd as L
+
+ROUTE_KEYS = ("topk_ids", "counts", "offsets", "sorted_pairs", "pair_rows")
+
+
+def to_dev_bits(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """bf16 bit patterns (uint16) -> int16 tensor on the device."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+def from_dev_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def route_gpu(d: L.LilyMoeDims, logits: np.ndarray, device="cuda"):
+    lg = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).to(device)
+    r = L.alloc_routing(d, device)
+    L.lily_moe_route(d, lg, r)
+    torch.cuda.synchronize()
+    return r
+
+
+def routing_to_host(r: L.Routing) -> dict:
+    out = {n: getattr(r, n).cpu().numpy() for n in L.ROUTING_FIELDS}
+    nb = int(out["num_blocks"][0])
+    out["block_expert"] = out["block_expert"][:nb]
+    out["block_row0"] = out["block_row0"][:nb]
+    return out
+
+
+def compare_routing(gpu: dict, ref: dict) -> None:
+    for k in ROUTE_KEYS:
+        assert np.array_equal(gpu[k], ref[k]), f"routing {k} differs at " \
+            f"{np.argwhere(np.asarray(gpu[k]) != np.asarray(ref[k]))[:5].tolist()}"
+    assert int(gpu["num_blocks"][0]) == int(ref["num_blocks"][0]), "num_blocks"
+    assert np.array_equal(gpu["block_expert"], ref["block_expert"]), "block_expert"
+    assert np.array_equal(gpu["block_row0"], ref["block_row0"]), "block_row0"
+    assert np.max(np.abs(gpu["topk_w"] - ref["topk_w"])) <= 2e-6, "topk_w"
+
+
+def forward_gpu(d: L.LilyMoeDims, w: L.Weights, x: torch.Tensor, r: L.Routing,
+                poison: bool = True, device="cuda") -> torch.Tensor:
+    ws = L.alloc_workspace(d, device)
+    if poison:  # NaN in every byte pattern: reads of unwritten workspace show up
+        ws.fill_(0xFF)
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device=device)
+    out.fill_(-1)
+    L.lily_moe_forward(d, w, x, r, out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def output_error(gpu_bits: np.ndarray, ref_acc: np.ndarray) -> float:
+    """max over elements of |gpu - ref| / (1e-2 * (|ref| + RMS(ref))): <= 1 passes."""
+    g = bf16_bits_to_f64(gpu_bits)
+    ref = ref_acc.astype(np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - ref) / (1e-2 * (np.abs(ref) + rms))))

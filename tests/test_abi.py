@@ -1,0 +1,141 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented codes before
+anything is enqueued (no GPU needed: no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_grouped_gemm_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lily_moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from int4_grouped_gemm_amd import build
+        build.build()
+    return L.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lily_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned; never dereferenced on these paths
+
+
+def good_dims(**kw):
+    d = dict(T=64, H=256, F=128, E=16, topk=2, group=64, tile_m=64)
+    d.update(kw)
+    return L.LilyMoeDims(**d)
+
+
+def routing(fake=FAKE, **over):
+    vals = {n: fake + 4096 * i for i, n in enumerate(L.ROUTING_FIELDS)}
+    vals.update(over)
+    return L.LilyMoeRouting(**vals)
+
+
+def weights(**over):
+    w = {n: L.LilyW4(FAKE, FAKE + 256, FAKE + 512) for n in
+         ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")}
+    w.update(over)
+    return L.LilyMoeWeights(**w)
+
+
+def call_route(lib, d, logits=FAKE, r=None):
+    r = r or routing()
+    return lib.lily_moe_route(ctypes.byref(d), logits, ctypes.byref(r), None)
+
+
+def call_forward(lib, d, w=None, x=FAKE, r=None, out=FAKE, ws=FAKE, nbytes=1 << 40):
+    w = w or weights()
+    r = r or routing()
+    return lib.lily_moe_forward(ctypes.byref(d), ctypes.byref(w), x, ctypes.byref(r), out, ws,
+                                nbytes, None)
+
+
+def test_size_queries(lib):
+    d = good_dims(T=2048, H=2048, F=512, E=256, topk=8, tile_m=64)
+    assert lib.lily_moe_max_blocks(ctypes.byref(d)) == 2048 * 8 // 64 + 256
+    rows = 2048 * 9
+    assert lib.lily_moe_workspace_bytes(ctypes.byref(d)) == rows * 512 * 2 + rows * 2048 * 4
+    d = good_dims(T=1, E=256, topk=8, tile_m=64)
+    assert lib.lily_moe_max_blocks(ctypes.byref(d)) == 1 + 8
+    bad = good_dims(T=0)
+    assert lib.lily_moe_max_blocks(ctypes.byref(bad)) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_moe_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(T=0), L.LILY_ERR_INVALID_ARG, "T = 0"),
+    (dict(E=0), L.LILY_ERR_INVALID_ARG, "E = 0"),
+    (dict(topk=0), L.LILY_ERR_INVALID_ARG, "topk"),
+    (dict(topk=17), L.LILY_ERR_INVALID_ARG, "topk"),
+    (dict(group=32), L.LILY_ERR_INVALID_ARG, "group"),
+    (dict(H=100), L.LILY_ERR_INVALID_ARG, "H = 100"),
+    (dict(F=0), L.LILY_ERR_INVALID_ARG, "F = 0"),
+    (dict(tile_m=0), L.LILY_ERR_INVALID_ARG, "tile_m"),
+    (dict(E=600, topk=8), L.LILY_ERR_UNSUPPORTED, "E = 600"),
+    (dict(E=128, topk=65), L.LILY_ERR_UNSUPPORTED, "topk = 65"),
+])
+def test_route_rejects_bad_dims(lib, kw, code, text):
+    assert call_route(lib, good_dims(**kw)) == code
+    assert text in lib.lily_last_error().decode()
+
+
+def test_route_rejects_pointers(lib):
+    assert call_route(lib, good_dims(), logits=None) == L.LILY_ERR_INVALID_ARG
+    assert "logits" in lib.lily_last_error().decode()
+    assert call_route(lib, good_dims(), logits=FAKE + 4) == L.LILY_ERR_INVALID_ARG
+    assert "aligned" in lib.lily_last_error().decode()
+    for n in L.ROUTING_FIELDS:
+        assert call_route(lib, good_dims(), r=routing(**{n: None})) == L.LILY_ERR_INVALID_ARG
+        assert n in lib.lily_last_error().decode()
+    assert lib.lily_moe_route(ctypes.byref(good_dims()), FAKE, None, None) == \
+        L.LILY_ERR_INVALID_ARG
+    assert lib.lily_moe_route(None, FAKE, ctypes.byref(routing()), None) == L.LILY_ERR_INVALID_ARG
+
+
+def test_forward_rejects(lib):
+    assert call_forward(lib, good_dims(tile_m=48)) == L.LILY_ERR_UNSUPPORTED
+    assert call_forward(lib, good_dims(H=192)) == L.LILY_ERR_UNSUPPORTED
+    assert call_forward(lib, good_dims(), x=None) == L.LILY_ERR_INVALID_ARG
+    assert call_forward(lib, good_dims(), out=FAKE + 2) == L.LILY_ERR_INVALID_ARG
+    assert call_forward(lib, good_dims(), ws=None) == L.LILY_ERR_INVALID_ARG
+    for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        w = weights(**{n: L.LilyW4(FAKE, None, FAKE)})
+        assert call_forward(lib, good_dims(), w=w) == L.LILY_ERR_INVALID_ARG
+        assert n in lib.lily_last_error().decode()
+    d = good_dims()
+    need = lib.lily_moe_workspace_bytes(ctypes.byref(d))
+    assert call_forward(lib, d, nbytes=need - 1) == L.LILY_ERR_WORKSPACE
+    assert str(need) in lib.lily_last_error().decode()
+    assert lib.lily_moe_forward(ctypes.byref(d), None, FAKE, ctypes.byref(routing()), FAKE, FAKE,
+                                need, None) == L.LILY_ERR_INVALID_ARG
+
+
+def test_residual_norm_rejects(lib):
+    assert lib.lily_residual_norm(0, 256, FAKE, FAKE, FAKE, 1e-6, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_residual_norm(4, 250, FAKE, FAKE, FAKE, 1e-6, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_residual_norm(4, 256, None, FAKE, FAKE, 1e-6, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_residual_norm(4, 256, FAKE, FAKE, FAKE, -1.0, None) == L.LILY_ERR_INVALID_ARG
+
+
+def test_binding_raises(lib):
+    with pytest.raises(L.LilyError) as ei:
+        L.lily_moe_max_blocks(good_dims(topk=99))
+    assert ei.value.code == L.LILY_ERR_INVALID_ARG
