@@ -1,0 +1,228 @@
+"""Benchmark of the int4 grouped-GEMM MoE layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch: lily_moe_route
+(top-k, softmax, histogram, scan, scatter, block map) then the three stages
+of lily_moe_forward (gate/up + SwiGLU, down, combine) for one MoE layer of
+T = 2048 tokens (H 2048, F 512, 256 experts top-8 + 1 shared, int4 g64,
+router logits N(0,1) plus a Zipf(1.1) log-bias per expert). Steps cycle
+through several distinct layer weight sets (8 by default, 3.6 GB) so that
+the weights stream from HBM instead of the on-package cache. Inputs are
+resident in HBM before timing starts.
+
+Prints ONE JSON line. ``value`` is MoE-layer tokens/s = T / (seconds per
+step), timed with the wall clock between two device synchronisations.
+``roofline`` reports the dominant kernel: its algorithmic flops (or bytes)
+per launch over its average duration from HIP events recorded on the launch
+stream around every launch in the timed region. ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer prefill tokens/s (T=2048, int4 g64); % of HBM / MFMA peak"
+WORKLOAD = "prefill2048_zipf"
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill2048_zipf.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "int4_grouped_gemm_amd", "csrc", f)
+                  for f in ("gemm_w4.hip", "route.hip", "common.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer weight sets cycled")
+    ap.add_argument("--tile-m", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens of layer 0 the CPU oracle computes for the baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 256 MiB device copy (twice) so that "
+                         "profiler byte counters can be scaled against a known size")
+    return ap.parse_args()
+
+
+def stage_work(cfg, P):
+    """Algorithmic work per launch of each stage (flops for GEMMs, bytes
+    for the memory-bound stages)."""
+    rows = P + cfg.T
+    return {
+        "route": ("hbm", cfg.T * cfg.E * 4 + P * 4 * 4 + cfg.T * cfg.k * 4),
+        "gate_up": ("mfma", 2.0 * rows * cfg.H * 2 * cfg.F),
+        "down": ("mfma", 2.0 * rows * cfg.F * cfg.H),
+        "combine": ("hbm", rows * cfg.H * 4 + cfg.T * cfg.H * 2 + P * 8),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the layer is a single-GPU kernel path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int4_grouped_gemm_amd as L
+    from synth import inputs as S
+
+    L.load()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[WORKLOAD]
+    d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, args.tile_m)
+    P = cfg.T * cfg.k
+
+    # ---- inputs, resident in HBM before timing
+    t_gen = time.time()
+    weights, logits = [], []
+    for layer in range(args.layers):
+        weights.append(L.weights_from_host(S.layer_weights(cfg, layer), dev))
+        logits.append(torch.from_numpy(S.router_logits(cfg, layer)).to(dev))
+    x = torch.from_numpy(S.activations(cfg).view(np.int16)).to(dev)
+    routing = L.alloc_routing(d, dev)
+    ws = L.alloc_workspace(d, dev)
+    h, y = L.workspace_views(d, ws)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    stages = ("route", "gate_up", "down", "combine")
+
+    def step(i, ev=None):
+        layer = i % args.layers
+        w = weights[layer]
+        if ev is not None:
+            ev[0].record(stream)
+        L.lily_moe_route(d, logits[layer], routing, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        L.lily_moe_gate_up(d, w, x, routing, h, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        L.lily_moe_down(d, w, h, routing, y, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        L.lily_moe_combine(d, y, routing, out, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = cfg.T / ((t1 - t0) / args.steps)
+    stage_ms = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
+                for j, s in enumerate(stages)}
+
+    work = stage_work(cfg, P)
+    dom = max(stages, key=lambda s: stage_ms[s])
+    bound, amount = work[dom]
+    if bound == "mfma":
+        achieved = amount / (stage_ms[dom] * 1e-3) / 1e12
+        peak, unit = PEAK_MFMA_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = amount / (stage_ms[dom] * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("stage") == dom \
+                and tr.get("tile_m") == args.tile_m:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom}
+
+    # whole-layer fractions: useful flops and the weight bytes one layer must read
+    counts = routing.counts.cpu().numpy()
+    used = int((counts > 0).sum()) + 1
+    w_bytes = used * 3 * cfg.H * cfg.F * (0.5 + 4.0 / 64)
+    layer_flops = 2.0 * 3 * cfg.H * cfg.F * (P + cfg.T)
+    step_s = ms_per_step * 1e-3
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "topk": cfg.k,
+            "shared_experts": 1, "group": 64, "tile_m": args.tile_m,
+            "layer_weight_sets": args.layers,
+            "routing": "logits N(0,1) + per-expert Zipf(1.1) log-bias",
+            "weights": "int4 q~U{0..15}, bf16 scale~U(0.005,0.02), bf16 bias~N(0,0.01)",
+        },
+        "layer": {
+            "mfma_frac": round(layer_flops / step_s / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+            "hbm_weight_frac": round(w_bytes / step_s / 1e9 / PEAK_HBM_GBS, 4),
+            "experts_touched": used,
+        },
+        "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle import build as _ob  # noqa: F401  (oracle is built by __graft_entry__.build)
+        lw = S.layer_weights(cfg, 0)
+        lg = S.router_logits(cfg, 0)
+        xs = S.activations(cfg)
+        ntok = min(args.cpu_tokens, cfg.T)
+        c0 = time.perf_counter()
+        rr = oracle.route(lg, cfg.k, args.tile_m)
+        oracle.forward(xs, rr["topk_ids"], rr["topk_w"], oracle.getter_from_layer(lw),
+                       cfg.H, cfg.F, cfg.E, tokens=list(range(ntok)))
+        c1 = time.perf_counter()
+        result["cpu_baseline"] = {
+            "value": round(ntok / (c1 - c0), 2), "unit": "tokens/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"route of all {cfg.T} tokens + forward of {ntok} tokens of layer 0 "
+                      f"(dequant of the experts they use included), {c1 - c0:.1f} s",
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -138,10 +138,30 @@ int lily_moe_route(const lily_moe_dims* dims, const float* logits,
    are ignored). The routing is trusted (ids in range, block map as produced
    by lily_moe_route). Run-to-run deterministic: no floating-point atomics.
    Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (tile_m not 32/64/128,
-   H or F not a multiple of 128), LILY_ERR_WORKSPACE, LILY_ERR_HIP. */
+   H not a multiple of 256, F not a multiple of 128), LILY_ERR_WORKSPACE,
+   LILY_ERR_HIP. */
 int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
                      const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* The three stages of lily_moe_forward, callable one at a time (for example
+   to time each stage). lily_moe_forward runs exactly these kernels in this
+   order on the workspace. P = T * topk; rows 0..P-1 are the routed (token,
+   expert) pairs in expert order (row r = pair sorted_pairs[r]); rows
+   P..P+T-1 are the shared expert's rows for tokens 0..T-1.
+   lily_moe_gate_up: h[r] = bf16(silu(x Wg^T) * (x Wu^T)) with the weights
+     dequantised tile by tile on chip; h: bf16 bits [P + T, F].
+   lily_moe_down: y[r] = h[r] Wd^T in fp32; y: fp32 [P + T, H].
+   lily_moe_combine: out[t] = bf16(y[P + t] + sum_j topk_w[t, j] *
+     y[pair_rows[t * topk + j]]), fp32 sum in slot order; out: bf16 [T, H].
+   Errors as for lily_moe_forward (no workspace check). */
+int lily_moe_gate_up(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                     const uint16_t* x, const lily_moe_routing* routing, uint16_t* h,
+                     void* stream);
+int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights, const uint16_t* h,
+                  const lily_moe_routing* routing, float* y, void* stream);
+int lily_moe_combine(const lily_moe_dims* dims, const float* y, const lily_moe_routing* routing,
+                     uint16_t* out, void* stream);
 
 /* Residual stream between stacked MoE layers (the pages describe a stack of
    layers but not this glue; the reading is a pre-norm residual with a

@@ -24,7 +24,8 @@ LILY_ERR_WORKSPACE = -3
 LILY_ERR_HIP = -4
 
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_moe_route",
-           "lily_moe_forward", "lily_residual_norm", "lily_last_error")
+           "lily_moe_forward", "lily_moe_gate_up", "lily_moe_down", "lily_moe_combine",
+           "lily_residual_norm", "lily_last_error")
 
 
 class LilyMoeDims(ctypes.Structure):
@@ -80,6 +81,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_moe_forward.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
                                      P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.lily_moe_gate_up.restype = ctypes.c_int
+    lib.lily_moe_gate_up.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
+                                     P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_moe_down.restype = ctypes.c_int
+    lib.lily_moe_down.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
+                                  P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_moe_combine.restype = ctypes.c_int
+    lib.lily_moe_combine.argtypes = [P(LilyMoeDims), ctypes.c_void_p, P(LilyMoeRouting),
+                                     ctypes.c_void_p, ctypes.c_void_p]
     lib.lily_residual_norm.restype = ctypes.c_int
     lib.lily_residual_norm.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
@@ -141,8 +151,11 @@ class Weights:
     sh_down: W4
 
     def c(self) -> LilyMoeWeights:
-        return LilyMoeWeights(*(getattr(self, n).c() for n in
-                                ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")))
+        # device pointers do not change while the tensors live: build once
+        if getattr(self, "_c", None) is None:
+            self._c = LilyMoeWeights(*(getattr(self, n).c() for n in
+                                       ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")))
+        return self._c
 
 
 @dataclasses.dataclass
@@ -158,7 +171,9 @@ class Routing:
     num_blocks: torch.Tensor
 
     def c(self) -> LilyMoeRouting:
-        return LilyMoeRouting(*(_ptr(getattr(self, n)) for n in ROUTING_FIELDS))
+        if getattr(self, "_c", None) is None:
+            self._c = LilyMoeRouting(*(_ptr(getattr(self, n)) for n in ROUTING_FIELDS))
+        return self._c
 
 
 def lily_moe_max_blocks(d: LilyMoeDims) -> int:
@@ -194,6 +209,28 @@ def lily_moe_forward(d: LilyMoeDims, weights: Weights, x, routing: Routing, out,
     _check(rc, lib)
 
 
+def lily_moe_gate_up(d: LilyMoeDims, weights: Weights, x, routing: Routing, h,
+                     stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_gate_up(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(x),
+                              ctypes.byref(routing.c()), _ptr(h), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_down(d: LilyMoeDims, weights: Weights, h, routing: Routing, y, stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_down(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(h),
+                           ctypes.byref(routing.c()), _ptr(y), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_combine(d: LilyMoeDims, y, routing: Routing, out, stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_combine(ctypes.byref(d), _ptr(y), ctypes.byref(routing.c()), _ptr(out),
+                              _stream(stream))
+    _check(rc, lib)
+
+
 def lily_residual_norm(T: int, H: int, r, out, x_next, eps: float = 1e-6, stream=None) -> None:
     lib = load()
     rc = lib.lily_residual_norm(T, H, _ptr(r), _ptr(out), _ptr(x_next), eps, _stream(stream))
@@ -222,6 +259,18 @@ def alloc_routing(d: LilyMoeDims, device="cuda") -> Routing:
 
 def alloc_workspace(d: LilyMoeDims, device="cuda") -> torch.Tensor:
     return torch.empty(lily_moe_workspace_bytes(d), dtype=torch.uint8, device=device)
+
+
+def workspace_views(d: LilyMoeDims, ws: torch.Tensor):
+    """(h, y) views of a forward workspace, laid out as the library uses it:
+    h bf16 bits [P + T, F] at offset 0, y fp32 [P + T, H] at the next
+    256-byte boundary."""
+    rows = d.T * d.topk + d.T
+    hb = rows * d.F * 2
+    y0 = (hb + 255) // 256 * 256
+    h = ws[:hb].view(torch.int16).view(rows, d.F)
+    y = ws[y0:y0 + rows * d.H * 4].view(torch.float32).view(rows, d.H)
+    return h, y
 
 
 def weights_from_host(lw, device="cuda") -> Weights:

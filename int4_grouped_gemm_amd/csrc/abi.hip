@@ -25,10 +25,14 @@ int check_launch(const char* what) {
 
 int launch_route(const lily_moe_dims& d, const float* logits, const lily_moe_routing& r,
                  hipStream_t stream);
-int launch_forward(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
-                   const lily_moe_routing& r, uint16_t* out, void* ws, int max_blocks,
-                   hipStream_t stream);
+int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+                   const lily_moe_routing& r, int max_blocks, uint16_t* h, hipStream_t stream);
+int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* h,
+                const lily_moe_routing& r, int max_blocks, float* y, hipStream_t stream);
+int launch_combine(const lily_moe_dims& d, const float* y, const lily_moe_routing& r,
+                   uint16_t* out, hipStream_t stream);
 size_t forward_workspace_bytes(const lily_moe_dims& d);
+void forward_workspace_split(const lily_moe_dims& d, void* ws, uint16_t** h, float** y);
 int launch_residual_norm(int T, int H, float* r, const uint16_t* out, uint16_t* x_next,
                          float eps, hipStream_t stream);
 
@@ -90,6 +94,27 @@ static int check_w4(const lily_w4& w, const char* name) {
     return LILY_OK;
 }
 
+static int check_forward_args(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                              const lily_moe_routing* routing) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!weights) return set_error(LILY_ERR_INVALID_ARG, "weights is NULL");
+    if ((rc = check_w4(weights->gate, "gate")) || (rc = check_w4(weights->up, "up")) ||
+        (rc = check_w4(weights->down, "down")) || (rc = check_w4(weights->sh_gate, "sh_gate")) ||
+        (rc = check_w4(weights->sh_up, "sh_up")) || (rc = check_w4(weights->sh_down, "sh_down")))
+        return rc;
+    rc = check_routing(routing);
+    if (rc) return rc;
+    if (dims->tile_m != 32 && dims->tile_m != 64 && dims->tile_m != 128)
+        return set_error(LILY_ERR_UNSUPPORTED, "tile_m = %d; forward supports 32, 64, 128",
+                         dims->tile_m);
+    if (dims->H % 256)
+        return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 256", dims->H);
+    if (dims->F % 128)
+        return set_error(LILY_ERR_UNSUPPORTED, "F = %d must be a multiple of 128", dims->F);
+    return LILY_OK;
+}
+
 }  // namespace lily
 
 using namespace lily;
@@ -120,22 +145,10 @@ int lily_moe_route(const lily_moe_dims* dims, const float* logits,
 int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
                      const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
                      void* workspace, size_t workspace_bytes, void* stream) {
-    int rc = check_dims(dims);
+    int rc = check_forward_args(dims, weights, routing);
     if (rc) return rc;
-    if (!weights) return set_error(LILY_ERR_INVALID_ARG, "weights is NULL");
-    if ((rc = check_w4(weights->gate, "gate")) || (rc = check_w4(weights->up, "up")) ||
-        (rc = check_w4(weights->down, "down")) || (rc = check_w4(weights->sh_gate, "sh_gate")) ||
-        (rc = check_w4(weights->sh_up, "sh_up")) || (rc = check_w4(weights->sh_down, "sh_down")))
-        return rc;
     REQUIRE_PTR(x);
     REQUIRE_PTR(out);
-    rc = check_routing(routing);
-    if (rc) return rc;
-    if (dims->tile_m != 32 && dims->tile_m != 64 && dims->tile_m != 128)
-        return set_error(LILY_ERR_UNSUPPORTED, "tile_m = %d; forward supports 32, 64, 128",
-                         dims->tile_m);
-    if (dims->H % 128 || dims->F % 64)
-        return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 128", dims->H);
     const size_t need = forward_workspace_bytes(*dims);
     if (!workspace) return set_error(LILY_ERR_INVALID_ARG, "workspace is NULL");
     if (!aligned16(workspace))
@@ -143,8 +156,47 @@ int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
     if (workspace_bytes < need)
         return set_error(LILY_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
                          workspace_bytes, need);
-    return launch_forward(*dims, *weights, x, *routing, out, workspace, max_blocks_of(*dims),
+    uint16_t* h;
+    float* y;
+    forward_workspace_split(*dims, workspace, &h, &y);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int mb = max_blocks_of(*dims);
+    if ((rc = launch_gate_up(*dims, *weights, x, *routing, mb, h, s))) return rc;
+    if ((rc = launch_down(*dims, *weights, h, *routing, mb, y, s))) return rc;
+    return launch_combine(*dims, y, *routing, out, s);
+}
+
+int lily_moe_gate_up(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                     const uint16_t* x, const lily_moe_routing* routing, uint16_t* h,
+                     void* stream) {
+    int rc = check_forward_args(dims, weights, routing);
+    if (rc) return rc;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(h);
+    return launch_gate_up(*dims, *weights, x, *routing, max_blocks_of(*dims), h,
                           reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights, const uint16_t* h,
+                  const lily_moe_routing* routing, float* y, void* stream) {
+    int rc = check_forward_args(dims, weights, routing);
+    if (rc) return rc;
+    REQUIRE_PTR(h);
+    REQUIRE_PTR(y);
+    return launch_down(*dims, *weights, h, *routing, max_blocks_of(*dims), y,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_combine(const lily_moe_dims* dims, const float* y, const lily_moe_routing* routing,
+                     uint16_t* out, void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    rc = check_routing(routing);
+    if (rc) return rc;
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(out);
+    if (dims->H % 4) return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 4", dims->H);
+    return launch_combine(*dims, y, *routing, out, reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_residual_norm(int32_t T, int32_t H, float* r, const uint16_t* out, uint16_t* x_next,

@@ -40,6 +40,7 @@ struct GemmArgs {
     const int32_t* num_blocks;
     const int32_t* offsets;
     int max_blocks;
+    int shared_blocks;  // ceil(T / BM)
     int P, T;
     uint16_t* h_out;  // gate/up: h [P + T, N] bf16
     float* y_out;     // down: y [P + T, N] fp32
@@ -47,210 +48,301 @@ struct GemmArgs {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (a few ulp
+// of fp32, far below the bf16 rounding of h that follows).
+__device__ __forceinline__ float silu(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
 
-// 32 int4 weights (16 bytes, element 2i in the low nibble of byte i) ->
-// 32 bf16 as four 16-byte chunks: w = bf16(scale * q + bias).
-__device__ __forceinline__ void dequant32(const u32x4 qv, float s, float b, u32x4 out[4]) {
+// Eight int4 weights (one 32-bit word: element 2i in the low nibble of byte
+// i) -> four bf16x2 words of w = bf16(scale * q + bias), elements in order.
+// A byte 0x00..0x0F read as an OCP e4m3 value is exactly q * 2^-9 (exponent
+// field 0 or 1), so one v_cvt_pk_f32_fp8 widens two nibbles, and with
+// s512 = scale * 2^9 (exact) fma(s512, q * 2^-9, bias) is the same single
+// rounding of scale * q + bias as fma(scale, q, bias).
+__device__ __forceinline__ void dequant8(uint32_t v, float s512, float b, uint32_t out[4]) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const uint32_t lo = v & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+    const f2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const f2 e46 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const f2 e13 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const f2 e57 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    out[0] = pack_bf16x2(fmaf(s512, e02[0], b), fmaf(s512, e13[0], b));
+    out[1] = pack_bf16x2(fmaf(s512, e02[1], b), fmaf(s512, e13[1], b));
+    out[2] = pack_bf16x2(fmaf(s512, e46[0], b), fmaf(s512, e57[0], b));
+    out[3] = pack_bf16x2(fmaf(s512, e46[1], b), fmaf(s512, e57[1], b));
+}
+
+// Tile geometry. A workgroup has 4 wavefronts that split the output columns;
+// every wavefront covers all BM rows of the block. The workgroup owns 256
+// weight rows: for the gate/up GEMM 128 gate rows and the same 128 up rows
+// (so SwiGLU is local to a lane), for the down GEMM 256 rows of W_down.
+// Wavefront w takes two groups of 32 weight rows: gate/up -> gate rows
+// 32w.. and up rows 128+32w..; down -> rows 64w.. and 64w+32...
+//
+// Every operand travels global -> LDS with global_load_lds (no registers,
+// no compiler-managed waits), kNS k-steps in flight:
+//   A stage  [BM rows][64 bf16], 16-byte chunks XOR-swizzled by (row & 7);
+//   Q stage  [2 halves][256 rows][16 bytes] of int4 weights;
+//   SB ring  scales then biases of the 256 rows for two k-steps (4 bytes a
+//            row), refreshed every other k-step.
+// Each lane then dequantises its own 32 weights of a k-step from LDS into
+// MFMA operand registers (no weight is dequantised twice in a workgroup).
+//
+// K mapping inside a 64-wide k-step: lanes 0-31 (h = 0) hold k 0..31 and
+// lanes 32-63 (h = 1) hold k 32..63; MFMA step s (16 k) pairs elements
+// 8s..8s+7 of each half, for A and B alike. So a lane's A operand for step s
+// is the 16-byte chunk 4h + s of its row.
+constexpr int kGemmThreads = 256;
+constexpr int kGemmWaves = kGemmThreads / kWave;
+constexpr int kNS = 3;  // k-steps in flight through LDS
+constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
+
+template <bool GATED>
+struct GemmShape {
+    static constexpr int BN = GATED ? 128 : 256;  // output columns per workgroup
+};
+
+template <int BM>
+struct Lds {
+    static constexpr int A = BM * 128;          // bytes of one A stage
+    static constexpr int Q = 256 * 32;          // bytes of one weight stage
+    static constexpr int SB = 256 * 4 * 2;      // scales, then biases, two k-steps each
+    static constexpr int A_OFF = 0;
+    static constexpr int Q_OFF = kNS * A;
+    static constexpr int SB_OFF = Q_OFF + kNS * Q;
+    static constexpr int TOTAL = SB_OFF + 2 * SB;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One global -> LDS load per lane; lane l lands at lds_wave_base + l * size.
+__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
+}
+
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+// Workgroup barrier without the memory fences of __syncthreads (which would
+// drain every load in flight); the empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, bool GATED, int MIA>
+__device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int r0, int rows,
+                                          const uint16_t* const* a_src, const uint8_t* const* q_src,
+                                          const uint16_t* const* sb_src, const int* brow,
+                                          const int* col0) {
+    using Ld = Lds<BM>;
+    constexpr int NI = 2;
+    constexpr int N_A = MIA;  // A loads per wavefront per k-step (8 rows each)
+    constexpr int N_Q = 2;    // weight loads per wavefront per k-step
+    constexpr int N_SB = 2;   // scale/bias loads per wavefront per even k-step
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int h = lane / 32;
+    const int nk = args.K / 64;
+
+    auto issue = [&](int kt) {
+        const int buf = kt % kNS;
+        char* a_base = smem + Ld::A_OFF + buf * Ld::A;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t v = qv[w];  // 8 nibbles: elements 8w .. 8w+7
-        float f[8];
+        for (int j = 0; j < N_A; ++j)
+            dma16(a_src[j] + kt * 64, a_base + (32 * j + 8 * wave) * 128);
+        char* q_base = smem + Ld::Q_OFF + buf * Ld::Q;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = fmaf(s, (float)((v >> (4 * i)) & 0xFu), b);
-        out[w][0] = pack_bf16x2(f[0], f[1]);
-        out[w][1] = pack_bf16x2(f[2], f[3]);
-        out[w][2] = pack_bf16x2(f[4], f[5]);
-        out[w][3] = pack_bf16x2(f[6], f[7]);
+        for (int j = 0; j < N_Q; ++j)
+            dma16(q_src[j] + kt * 32, q_base + 64 * (2 * wave + j) * 16);
+        if ((kt & 1) == 0) {
+            char* sb_base = smem + Ld::SB_OFF + ((kt >> 1) & 1) * Ld::SB;
+#pragma unroll
+            for (int j = 0; j < N_SB; ++j)
+                dma4(sb_src[j] + kt, sb_base + 64 * (2 * wave + j) * 4);
+        }
+    };
+
+    f32x16 acc[MIA][NI];
+#pragma unroll
+    for (int i = 0; i < MIA; ++i)
+#pragma unroll
+        for (int g = 0; g < NI; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][g][r] = 0.0f;
+
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+        // Stage kt has landed once only the loads of stage kt + 1 are left.
+        if (kt + 1 >= nk) wait_vmcnt<0>();
+        else if (kt & 1) wait_vmcnt<N_A + N_Q + N_SB>();  // kt + 1 is even
+        else wait_vmcnt<N_A + N_Q>();
+        barrier_only();
+        if (kt + 2 < nk) issue(kt + 2);
+
+        const int buf = kt % kNS;
+        const char* Ab = smem + Ld::A_OFF + buf * Ld::A;
+        const char* Qb = smem + Ld::Q_OFF + buf * Ld::Q;
+        const char* Sb = smem + Ld::SB_OFF + ((kt >> 1) & 1) * Ld::SB + (kt & 1) * 2;
+        bf16x8 bfr[NI][4];
+#pragma unroll
+        for (int g = 0; g < NI; ++g) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(Qb + (h * 256 + brow[g]) * 16);
+            const float s512 = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + brow[g] * 4)) * 512.0f;
+            const float b = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + 1024 + brow[g] * 4));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                uint32_t w[4];
+                dequant8(q[s], s512, b, w);
+                bfr[g][s] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int chunk = 4 * h + s;
+#pragma unroll
+            for (int i = 0; i < MIA; ++i) {
+                const int row = 32 * i + lane % 32;
+                const bf16x8 af = *reinterpret_cast<const bf16x8*>(Ab + row * 128 + swz(row, chunk) * 16);
+#pragma unroll
+                for (int g = 0; g < NI; ++g)
+                    acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[g][s], acc[i][g], 0, 0, 0);
+            }
+        }
+        wait_lgkmcnt0();  // this wavefront's LDS reads of the stage are done
+    }
+
+    // Epilogue. C layout of a 32x32 tile: lane l, register r holds row
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32.
+#pragma unroll
+    for (int i = 0; i < MIA; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+            if (row < rows) {
+                const size_t orow = (size_t)(r0 + row) * args.N;
+                if (GATED) {
+                    const float g = acc[i][0][r];
+                    const float u = acc[i][1][r];
+                    args.h_out[orow + col0[0] + lane % 32] = float_to_bf16_bits(silu(g) * u);
+                } else {
+#pragma unroll
+                    for (int g = 0; g < NI; ++g) args.y_out[orow + col0[g] + lane % 32] = acc[i][g][r];
+                }
+            }
+        }
     }
 }
 
-template <int BM, int BN, int NWM, int NWN, bool GATED>
-__global__ void __launch_bounds__(NWM * NWN * kWave) grouped_w4_gemm(GemmArgs args) {
-    constexpr int NT = NWM * NWN * kWave;
-    constexpr int NB = GATED ? 2 : 1;
-    constexpr int WM = BM / NWM, WN = BN / NWN;
-    constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int A_CHUNKS = BM * 8;          // 16-byte chunks of bf16 per A k-step
-    constexpr int A_PER_T = A_CHUNKS / NT;
-    constexpr int B_CHUNKS = NB * BN * 2;     // 16-byte chunks of int4 per B k-step
-    constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
-    static_assert(A_CHUNKS % NT == 0, "A tile must split evenly");
-    static_assert(MI >= 1 && NI >= 1, "wave tile must be at least 32x32");
-
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * 64];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BN * 64];
+template <int BM, bool GATED>
+__global__ void __launch_bounds__(kGemmThreads, 2) moe_w4_gemm(GemmArgs args) {
+    constexpr int BN = GemmShape<GATED>::BN;
+    constexpr int MI = BM / 32;
+    __shared__ __attribute__((aligned(16))) char smem[Lds<BM>::TOTAL];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
-    const int wm0 = (wave / NWN) * WM;
-    const int wn0 = (wave % NWN) * WN;
-    const int n0 = blockIdx.x * BN;
+
+    // Tiles are (block, n-tile) pairs: the routed blocks of the block map,
+    // then the shared expert's blocks; n-tiles vary fastest. Workgroups are
+    // dispatched to the 8 XCDs round-robin, so workgroup L runs on XCD L % 8;
+    // each XCD takes a contiguous range of the live tiles, so that the
+    // n-tiles of a block (same A rows) and consecutive blocks of an expert
+    // (same weights) meet in one L2.
+    const int n_tiles = args.N / BN;
+    const int live = (args.num_blocks[0] + args.shared_blocks) * n_tiles;
+    const int per_xcd = (live + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int tile = (blockIdx.x % kXcds) * per_xcd + slot;
+    if (slot >= per_xcd || tile >= live) return;
+    const int blk = tile / n_tiles;
+    const int n0 = (tile % n_tiles) * BN;
 
     // Which rows, which expert.
-    const int bid = blockIdx.y;
     int r0, r_end;
     bool shared;
     int e = 0;
-    if (bid < args.max_blocks) {
-        if (bid >= args.num_blocks[0]) return;
-        e = args.block_expert[bid];
-        r0 = args.block_row0[bid];
+    if (blk < args.num_blocks[0]) {
+        e = args.block_expert[blk];
+        r0 = args.block_row0[blk];
         r_end = args.offsets[e + 1];
         shared = false;
     } else {
-        r0 = args.P + (bid - args.max_blocks) * BM;
+        r0 = args.P + (blk - args.num_blocks[0]) * BM;
         r_end = args.P + args.T;
         shared = true;
     }
     const int rows = min(BM, r_end - r0);
     const int K = args.K;
-    const int nk = K / 64;
 
-    // Per-thread A sources (row pointers are fixed over K).
-    const uint16_t* a_src[A_PER_T];
+    // A loads: load j of wavefront w fills LDS rows 32j + 8w + lane/8,
+    // physical chunk lane%8, which holds logical chunk (lane%8) ^ (row & 7).
+    // Rows past the block read the block's first row: their products land in
+    // output rows that are never stored.
+    const uint16_t* a_src[MI];
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / 8;
-        a_src[i] = nullptr;
-        if (row < rows) {
-            const int r = r0 + row;
-            int src_row = r;
-            if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
-            a_src[i] = args.a + (size_t)src_row * K + (c % 8) * 8;
-        }
+    for (int j = 0; j < MI; ++j) {
+        const int row = 32 * j + 8 * wave + lane / 8;
+        const int r = r0 + (row < rows ? row : 0);
+        int src_row = r;
+        if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
+        a_src[j] = args.a + (size_t)src_row * K + (((lane % 8) ^ (row & 7)) * 8);
     }
-    // Per-thread B sources.
-    const uint8_t* b_q[B_PER_T];
-    const uint16_t* b_s[B_PER_T];
-    const uint16_t* b_b[B_PER_T];
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) {
-        const int c = tid + i * NT;
-        b_q[i] = nullptr;
-        if (c < B_CHUNKS) {
-            const int m = c / (BN * 2);
-            const int rr = (c % (BN * 2)) / 2;
-            const int half = c % 2;
-            const int n = n0 + rr;
-            const size_t mat = shared ? 0 : (size_t)e * args.N;
-            const uint8_t* qb = shared ? args.sq[m] : args.q[m];
-            const uint16_t* sb = shared ? args.ssc[m] : args.sc[m];
-            const uint16_t* bb = shared ? args.sbi[m] : args.bi[m];
-            b_q[i] = qb + (mat + n) * (K / 2) + half * 16;
-            b_s[i] = sb + (mat + n) * (K / 64);
-            b_b[i] = bb + (mat + n) * (K / 64);
-        }
-    }
-
-    u32x4 a_reg[A_PER_T];
-    u32x4 q_reg[B_PER_T];
-    uint16_t s_reg[B_PER_T], bb_reg[B_PER_T];
-
-    auto load_tile = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            if (a_src[i]) a_reg[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * 64);
-            else a_reg[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            if (b_q[i]) {
-                q_reg[i] = *reinterpret_cast<const u32x4*>(b_q[i] + kt * 32);
-                s_reg[i] = b_s[i][kt];
-                bb_reg[i] = b_b[i][kt];
-            }
-        }
+    // Weight row r_loc (0..255) of the workgroup: matrix and row.
+    const size_t mat = shared ? 0 : (size_t)e * args.N;
+    auto wq = [&](int r_loc) -> const uint8_t* {
+        const int m = GATED ? r_loc / 128 : 0;
+        const int n = GATED ? n0 + r_loc % 128 : n0 + r_loc;
+        return (shared ? args.sq[m] : args.q[m]) + (mat + n) * (K / 2);
     };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / 8;
-            *reinterpret_cast<u32x4*>(&As[row * 64 + swz(row, c % 8) * 8]) = a_reg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            const int c = tid + i * NT;
-            if (c < B_CHUNKS) {
-                const int m = c / (BN * 2);
-                const int rr = (c % (BN * 2)) / 2;
-                const int half = c % 2;
-                u32x4 w[4];
-                dequant32(q_reg[i], bf16_bits_to_float(s_reg[i]), bf16_bits_to_float(bb_reg[i]), w);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<u32x4*>(&Bs[m][rr * 64 + swz(rr, half * 4 + j) * 8]) = w[j];
-            }
-        }
+    auto wsb = [&](int r_loc, bool bias) -> const uint16_t* {
+        const int m = GATED ? r_loc / 128 : 0;
+        const int n = GATED ? n0 + r_loc % 128 : n0 + r_loc;
+        const uint16_t* base = bias ? (shared ? args.sbi[m] : args.bi[m])
+                                    : (shared ? args.ssc[m] : args.sc[m]);
+        return base + (mat + n) * (K / 64);
     };
-
-    f32x16 acc[NB][MI][NI];
+    // Weight loads: load j of wavefront w fills 16-byte slots 64(2w + j) +
+    // lane = (half, row) of the Q stage.
+    const uint8_t* q_src[2];
+    const uint16_t* sb_src[2];
 #pragma unroll
-    for (int m = 0; m < NB; ++m)
+    for (int j = 0; j < 2; ++j) {
+        const int ci = 64 * (2 * wave + j) + lane;
+        q_src[j] = wq(ci % 256) + (ci / 256) * 16;
+        sb_src[j] = wsb(ci % 256, ci >= 256);
+    }
+    int brow[2], col0[2];
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.0f;
-
-    load_tile(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < nk) load_tile(kt + 1);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int chunk = 2 * s + lane / 32;
-            bf16x8 af[MI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int row = wm0 + 32 * i + lane % 32;
-                af[i] = *reinterpret_cast<const bf16x8*>(&As[row * 64 + swz(row, chunk) * 8]);
-            }
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-#pragma unroll
-                for (int j = 0; j < NI; ++j) {
-                    const int col = wn0 + 32 * j + lane % 32;
-                    const bf16x8 bfr =
-                        *reinterpret_cast<const bf16x8*>(&Bs[m][col * 64 + swz(col, chunk) * 8]);
-#pragma unroll
-                    for (int i = 0; i < MI; ++i)
-                        acc[m][i][j] =
-                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[m][i][j], 0, 0, 0);
-                }
-            }
-        }
+    for (int g = 0; g < 2; ++g) {
+        brow[g] = GATED ? 128 * g + 32 * wave + lane % 32 : 64 * wave + 32 * g + lane % 32;
+        col0[g] = GATED ? n0 + 32 * wave : n0 + 64 * wave + 32 * g;
     }
 
-    // Epilogue. C layout of a 32x32 tile: lane l, register r holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int col = n0 + wn0 + 32 * j + lane % 32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm0 + 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (row < rows) {
-                    const size_t o = (size_t)(r0 + row) * args.N + col;
-                    if (GATED) {
-                        const float g = acc[0][i][j][r];
-                        const float u = acc[NB - 1][i][j][r];
-                        args.h_out[o] = float_to_bf16_bits(silu(g) * u);
-                    } else {
-                        args.y_out[o] = acc[0][i][j][r];
-                    }
-                }
-            }
-        }
-    }
+    // Only the 32-row sub-tiles that hold rows of the block are loaded and
+    // multiplied.
+    const int mia = (rows + 31) / 32;
+    if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
+    else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
+    else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
+    else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
 }
 
 // out[t] = bf16(y[P + t] + sum_j w[t, j] * y[pair_rows[t * topk + j]]), fp32,
@@ -290,25 +382,48 @@ size_t forward_workspace_bytes(const lily_moe_dims& d) {
     return align_up(rows * d.F * sizeof(uint16_t)) + align_up(rows * d.H * sizeof(float));
 }
 
-template <int BM>
-static int launch_gemms(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
-                        const lily_moe_routing& r, int max_blocks, uint16_t* h, float* y,
-                        hipStream_t stream) {
-    const int P = d.T * d.topk;
-    const int shared_blocks = (d.T + BM - 1) / BM;
+static GemmArgs routing_args(const lily_moe_dims& d, const lily_moe_routing& r, int max_blocks) {
     GemmArgs g{};
-    g.sorted_pairs = r.sorted_pairs;
     g.topk = d.topk;
     g.block_expert = r.block_expert;
     g.block_row0 = r.block_row0;
     g.num_blocks = r.num_blocks;
     g.offsets = r.offsets;
     g.max_blocks = max_blocks;
-    g.P = P;
+    g.P = d.T * d.topk;
     g.T = d.T;
+    return g;
+}
 
-    // gate/up + SwiGLU: N = F, K = H
+// Grid: enough workgroups for the largest possible block map (the live
+// count is only known on the device), a multiple of the XCD count.
+template <int BM, bool GATED>
+static dim3 gemm_grid(GemmArgs& g) {
+    g.shared_blocks = (g.T + BM - 1) / BM;
+    const long tiles = (long)(g.max_blocks + g.shared_blocks) * (g.N / GemmShape<GATED>::BN);
+    return dim3((unsigned)((tiles + kXcds - 1) / kXcds * kXcds));
+}
+
+template <int BM>
+static int launch_gate_up_bm(const lily_moe_dims& d, GemmArgs g, hipStream_t stream) {
+    const dim3 grid = gemm_grid<BM, true>(g);
+    hipLaunchKernelGGL((moe_w4_gemm<BM, true>), grid, dim3(kGemmThreads), 0, stream, g);
+    return check_launch("gate_up_gemm");
+}
+
+template <int BM>
+static int launch_down_bm(const lily_moe_dims& d, GemmArgs g, hipStream_t stream) {
+    const dim3 grid = gemm_grid<BM, false>(g);
+    hipLaunchKernelGGL((moe_w4_gemm<BM, false>), grid, dim3(kGemmThreads), 0, stream, g);
+    return check_launch("down_gemm");
+}
+
+// G1 + G2 (and the shared expert's rows): h = bf16(silu(x Wg^T) * (x Wu^T)).
+int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+                   const lily_moe_routing& r, int max_blocks, uint16_t* h, hipStream_t stream) {
+    GemmArgs g = routing_args(d, r, max_blocks);
     g.a = x;
+    g.sorted_pairs = r.sorted_pairs;
     g.q[0] = w.gate.q; g.sc[0] = w.gate.scale; g.bi[0] = w.gate.bias;
     g.q[1] = w.up.q;   g.sc[1] = w.up.scale;   g.bi[1] = w.up.bias;
     g.sq[0] = w.sh_gate.q; g.ssc[0] = w.sh_gate.scale; g.sbi[0] = w.sh_gate.bias;
@@ -316,55 +431,45 @@ static int launch_gemms(const lily_moe_dims& d, const lily_moe_weights& w, const
     g.N = d.F;
     g.K = d.H;
     g.h_out = h;
-    {
-        constexpr int BN = 64;
-        dim3 grid(d.F / BN, max_blocks + shared_blocks);
-        hipLaunchKernelGGL((grouped_w4_gemm<BM, BN, (BM >= 64 ? 2 : 1), 2, true>), grid,
-                           dim3((BM >= 64 ? 2 : 1) * 2 * kWave), 0, stream, g);
-        int rc = check_launch("gate_up_gemm");
-        if (rc) return rc;
+    switch (d.tile_m) {
+        case 32: return launch_gate_up_bm<32>(d, g, stream);
+        case 64: return launch_gate_up_bm<64>(d, g, stream);
+        case 128: return launch_gate_up_bm<128>(d, g, stream);
     }
-
-    // down: N = H, K = F
-    g.a = h;
-    g.sorted_pairs = nullptr;
-    g.q[0] = w.down.q; g.sc[0] = w.down.scale; g.bi[0] = w.down.bias;
-    g.q[1] = nullptr;  g.sc[1] = nullptr;      g.bi[1] = nullptr;
-    g.sq[0] = w.sh_down.q; g.ssc[0] = w.sh_down.scale; g.sbi[0] = w.sh_down.bias;
-    g.sq[1] = nullptr;     g.ssc[1] = nullptr;         g.sbi[1] = nullptr;
-    g.N = d.H;
-    g.K = d.F;
-    g.h_out = nullptr;
-    g.y_out = y;
-    {
-        constexpr int BN = 128;
-        dim3 grid(d.H / BN, max_blocks + shared_blocks);
-        hipLaunchKernelGGL((grouped_w4_gemm<BM, BN, (BM >= 64 ? 2 : 1), 2, false>), grid,
-                           dim3((BM >= 64 ? 2 : 1) * 2 * kWave), 0, stream, g);
-        int rc = check_launch("down_gemm");
-        if (rc) return rc;
-    }
-    return LILY_OK;
+    return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
 }
 
-int launch_forward(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
-                   const lily_moe_routing& r, uint16_t* out, void* ws, int max_blocks,
-                   hipStream_t stream) {
-    const size_t rows = (size_t)d.T * d.topk + d.T;
-    uint16_t* h = reinterpret_cast<uint16_t*>(ws);
-    float* y = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                        align_up(rows * d.F * sizeof(uint16_t)));
-    int rc;
+// G3 (and the shared expert's rows): y = h Wd^T in fp32.
+int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* h,
+                const lily_moe_routing& r, int max_blocks, float* y, hipStream_t stream) {
+    GemmArgs g = routing_args(d, r, max_blocks);
+    g.a = h;
+    g.q[0] = w.down.q; g.sc[0] = w.down.scale; g.bi[0] = w.down.bias;
+    g.sq[0] = w.sh_down.q; g.ssc[0] = w.sh_down.scale; g.sbi[0] = w.sh_down.bias;
+    g.N = d.H;
+    g.K = d.F;
+    g.y_out = y;
     switch (d.tile_m) {
-        case 32: rc = launch_gemms<32>(d, w, x, r, max_blocks, h, y, stream); break;
-        case 64: rc = launch_gemms<64>(d, w, x, r, max_blocks, h, y, stream); break;
-        case 128: rc = launch_gemms<128>(d, w, x, r, max_blocks, h, y, stream); break;
-        default: return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
+        case 32: return launch_down_bm<32>(d, g, stream);
+        case 64: return launch_down_bm<64>(d, g, stream);
+        case 128: return launch_down_bm<128>(d, g, stream);
     }
-    if (rc) return rc;
+    return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
+}
+
+// G5: weighted gather-combine.
+int launch_combine(const lily_moe_dims& d, const float* y, const lily_moe_routing& r,
+                   uint16_t* out, hipStream_t stream) {
     hipLaunchKernelGGL(combine_kernel, dim3(d.T), dim3(256), 0, stream, y, r.pair_rows, r.topk_w,
                        d.T * d.topk, d.H, d.topk, out);
     return check_launch("combine");
+}
+
+void forward_workspace_split(const lily_moe_dims& d, void* ws, uint16_t** h, float** y) {
+    const size_t rows = (size_t)d.T * d.topk + d.T;
+    *h = reinterpret_cast<uint16_t*>(ws);
+    *y = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                  align_up(rows * d.F * sizeof(uint16_t)));
 }
 
 }  // namespace lily

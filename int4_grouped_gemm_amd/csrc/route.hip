@@ -7,22 +7,22 @@
 //
 // Two kernels on one stream, no host synchronisation:
 //   route_topk:   one wavefront per token. Each lane holds E/64 logits as
-//                 64-bit keys (order-preserving float bits, then the inverted
-//                 expert index so that equal logits prefer the lower index);
-//                 k rounds of a wavefront arg-max pick the experts in
-//                 descending order; the softmax over the k picked logits runs
-//                 in slot order. Writes topk_ids and topk_w.
-//   route_finish: one 1024-thread workgroup. 16 wavefronts split the T*k
-//                 (token, slot) pairs into contiguous spans. Pass 1 builds a
-//                 per-wavefront histogram in LDS; ranks inside a span are
-//                 found 64 pairs at a time with ballots over the expert-id
-//                 bits (lanes holding the same expert form one group). Then
-//                 per-expert bases across wavefronts, the exclusive scans of
-//                 rows and of blocks, the block map, and pass 2, which
-//                 re-walks each span and writes every pair to
+//                 order-preserving 32-bit keys; each of k rounds takes the
+//                 wavefront maximum (DPP inside rows of 16 lanes, readlane
+//                 across rows) and, among the experts holding it, the lowest
+//                 index (ballots in expert order). The softmax over the k
+//                 picked logits runs in slot order. Writes topk_ids, topk_w.
+//   route_finish: one 1024-thread workgroup. 16 wavefronts split the
+//                 tokens into contiguous spans. Pass 1 counts rows per
+//                 expert per span (integer LDS atomics). Then per-expert
+//                 bases across spans, the exclusive scans of rows and of
+//                 blocks, the block map, and pass 2, which re-walks each span
+//                 in chunks of whole tokens and writes every pair to
 //                 offsets[e] + (rows of e in earlier spans) + (earlier pairs
-//                 of e in this span). This is a stable counting sort: no
-//                 atomics, so the result is deterministic and bit-exact.
+//                 of e in this span); inside a chunk the earlier pairs come
+//                 from a per-expert token bitmask. This is a stable counting
+//                 sort whose result does not depend on the order of any
+//                 atomic: deterministic and bit-exact.
 // For small T the top-k runs inside route_finish and the route is one launch.
 #include "common.hpp"
 
@@ -31,11 +31,13 @@ namespace lily {
 constexpr int kFinishThreads = 1024;
 constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kTopkThreads = 256;
-constexpr int kTopkTokensPerWave = 4;
+constexpr int kTopkTokensPerWave = 1;
 constexpr int kTopkTokensPerBlock = (kTopkThreads / kWave) * kTopkTokensPerWave;
 constexpr int kMaxPerLane = kMaxExperts / kWave;
 // Up to this many tokens the whole route runs in the single workgroup.
 constexpr int kFusedRouteMaxT = 64;
+// Chunks of 64 ids a wavefront loads at once in route_finish.
+constexpr int kBatch = 16;
 
 // Order-preserving map of a float to uint32; -0.0 is folded onto +0.0 so
 // that the two tie.
@@ -50,50 +52,71 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
     return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+// Maximum of a uint32 over the 64 lanes, returned uniformly: DPP within each
+// row of 16 lanes (quad swaps, then rotations by 4 and 8), then the four row
+// results through readlane. No LDS traffic.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false)); // row_ror 4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false)); // row_ror 8
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
 }
 
-// Top-k and softmax of one token by one wavefront.
+// Top-k and softmax of one token by one wavefront. Lane l holds the logits
+// of experts l, l + 64, ... as order-preserving keys; a taken expert's key
+// becomes 0, below every real key. Each round takes the wavefront maximum
+// and, among the experts holding it, the lowest index (ballots in expert
+// order).
 __device__ __forceinline__ void topk_one_token(const float* __restrict__ logits, int t, int E,
                                                int k, int32_t* __restrict__ topk_ids,
                                                float* __restrict__ topk_w) {
     const int lane = threadIdx.x % kWave;
     const float* row = logits + (size_t)t * E;
-    uint64_t key[kMaxPerLane];
+    const int nper = (E + kWave - 1) / kWave;
+    uint32_t key[kMaxPerLane];
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-        int e = lane + i * kWave;
-        key[i] = 0;  // below every real key
-        if (e < E) key[i] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~(uint32_t)e);
+        const int e = lane + i * kWave;
+        key[i] = (i < nper && e < E) ? ordered_bits(row[e]) : 0u;
     }
     int my_id = 0;
     float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
+        uint32_t best = 0;
 #pragma unroll
         for (int i = 0; i < kMaxPerLane; ++i)
-            if (key[i] == best) key[i] = 0;  // unique: the low word names the expert
+            if (i < nper) best = max(best, key[i]);
+        best = wave_max_u32(best);
+        int e_sel = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) {
+            if (i >= nper) break;
+            const uint64_t hit = __ballot(key[i] == best);
+            if (hit) {
+                e_sel = i * kWave + (int)__ffsll((long long)hit) - 1;
+                break;
+            }
+        }
+        if (lane == e_sel % kWave) {
+#pragma unroll
+            for (int i = 0; i < kMaxPerLane; ++i)
+                if (i == e_sel / kWave) key[i] = 0u;
+        }
         if (lane == j) {
-            my_id = (int)(~(uint32_t)best);
-            my_l = from_ordered_bits((uint32_t)(best >> 32));
+            my_id = e_sel;
+            my_l = from_ordered_bits(best);
         }
     }
     // softmax over the selected logits, summed in slot order
     const float l0 = __shfl(my_l, 0, kWave);
     const float ex = expf(my_l - l0);
     float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += __shfl(ex, j, kWave);
+    for (int j = 0; j < k; ++j) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
     if (lane < k) {
         topk_ids[(size_t)t * k + lane] = my_id;
         topk_w[(size_t)t * k + lane] = ex / sum;
@@ -111,55 +134,56 @@ __global__ void __launch_bounds__(kTopkThreads) route_topk_kernel(
     }
 }
 
-// Lanes of the wavefront holding the same expert id as this lane (ids are
-// below 2^nbits; lanes with id < 0 match nobody).
-__device__ __forceinline__ uint64_t match_same(int id, int nbits) {
-    uint64_t m = __ballot(id >= 0);
-    for (int b = 0; b < nbits; ++b) {
-        uint64_t bit = __ballot(id >= 0 && ((id >> b) & 1));
-        m &= ((id >> b) & 1) ? bit : ~bit;
-    }
-    return id >= 0 ? m : 0ull;
-}
-
 __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     const float* __restrict__ logits, int T, int E, int k, int M, int fused_topk,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_rows, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ block_row0, int32_t* __restrict__ num_blocks) {
-    __shared__ int32_t hist[kFinishWaves][kMaxExperts];  // per-span rows, then bases
-    __shared__ int32_t s_off[kMaxExperts + 1];            // row offsets
-    __shared__ int32_t s_bst[kMaxExperts + 1];            // block starts
+    __shared__ int32_t hist[kFinishWaves][kMaxExperts];    // rows per span, then cursors
+    __shared__ uint32_t cmask[kFinishWaves][kMaxExperts];  // tokens of a chunk, per expert
+    __shared__ int32_t s_off[kMaxExperts + 1];             // row offsets
+    __shared__ int32_t s_bst[kMaxExperts + 1];             // block starts
     __shared__ int32_t s_wsum[2][kFinishWaves];
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
-    const int P = T * k;
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
 
     if (fused_topk) {
         for (int t = wave; t < T; t += kFinishWaves) topk_one_token(logits, t, E, k, topk_ids, topk_w);
         __threadfence_block();
     }
-    for (int i = tid; i < kFinishWaves * kMaxExperts; i += kFinishThreads) (&hist[0][0])[i] = 0;
+    for (int i = tid; i < kFinishWaves * kMaxExperts; i += kFinishThreads) {
+        (&hist[0][0])[i] = 0;
+        (&cmask[0][0])[i] = 0u;
+    }
     __syncthreads();
 
-    // Contiguous span of pairs per wavefront, a multiple of 64.
-    const int span = ((P + kFinishWaves - 1) / kFinishWaves + kWave - 1) / kWave * kWave;
-    const int p_begin = wave * span;
-    const int p_end = min(P, p_begin + span);
-    const uint64_t below = (1ull << lane) - 1ull;
+    // Chunks of tpc whole tokens (tpc * k <= 64 pairs, tpc <= 32); each
+    // wavefront owns a contiguous span of chunks, spans in token order.
+    const int tpc = min(32, kWave / k);
+    const int cpairs = tpc * k;
+    const int n_chunks = (T + tpc - 1) / tpc;
+    const int chunks_per_wave = (n_chunks + kFinishWaves - 1) / kFinishWaves;
+    const int t_begin = min(T, wave * chunks_per_wave * tpc);
+    const int t_end = min(T, t_begin + chunks_per_wave * tpc);
+    const int p_begin = t_begin * k;
+    const int p_end = t_end * k;
+    const bool lane_in_chunk = lane < cpairs;
 
-    // Pass 1: rows per expert in each span.
-    for (int c = p_begin; c < p_end; c += kWave) {
-        const int p = c + lane;
-        const int e = p < p_end ? topk_ids[p] : -1;
-        const uint64_t same = match_same(e, nbits);
-        if (e >= 0 && (same & below) == 0ull)  // lowest lane of its group
-            hist[wave][e] += __popcll(same);
+    // Pass 1: rows per expert in each span (integer LDS atomics: the totals
+    // do not depend on their order).
+    for (int c0 = p_begin; c0 < p_end; c0 += cpairs * kBatch) {
+        int ids[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int p = c0 + b * cpairs + lane;
+            ids[b] = (lane_in_chunk && p < p_end) ? topk_ids[p] : -1;
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            if (ids[b] >= 0) atomicAdd(&hist[wave][ids[b]], 1);
     }
     __syncthreads();
 
@@ -181,8 +205,8 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     // each thread owns one expert (E <= 512 < 1024 threads).
     {
         const int e = tid;
-        int v_rows = e < E ? s_off[e] : 0;
-        int v_blks = e < E ? s_bst[e] : 0;
+        const int v_rows = e < E ? s_off[e] : 0;
+        const int v_blks = e < E ? s_bst[e] : 0;
         int inc_r = v_rows, inc_b = v_blks;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
@@ -230,18 +254,37 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
         block_row0[b] = s_off[lo] + (b - s_bst[lo]) * M;
     }
 
-    // Pass 2: stable positions.
-    for (int c = p_begin; c < p_end; c += kWave) {
-        const int p = c + lane;
-        const int e = p < p_end ? topk_ids[p] : -1;
-        const uint64_t same = match_same(e, nbits);
-        if (e >= 0) {
-            const int base = hist[wave][e];
-            const int row = s_off[e] + base + __popcll(same & below);
-            sorted_pairs[row] = p;
-            pair_rows[p] = row;
-            // the highest lane of the group advances the span's cursor
-            if ((same >> lane) == 1ull) hist[wave][e] = base + __popcll(same);
+    // Pass 2: stable positions. The k experts of a token are distinct, so
+    // inside a chunk the pairs of one expert are ordered by token: a bit per
+    // token (atomic OR into cmask) gives each pair the number of earlier
+    // pairs of its expert in the chunk; the chunk's last such pair advances
+    // the span's cursor and clears the mask. LDS operations of a wavefront
+    // complete in program order.
+    const int tl = lane / k;  // token of this lane inside its chunk (< tpc <= 32)
+    for (int c0 = p_begin; c0 < p_end; c0 += cpairs * kBatch) {
+        int ids[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int p = c0 + b * cpairs + lane;
+            ids[b] = (lane_in_chunk && p < p_end) ? topk_ids[p] : -1;
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            if (c0 + b * cpairs >= p_end) break;
+            const int e = ids[b];
+            if (e >= 0) atomicOr(&cmask[wave][e], 1u << tl);
+            if (e >= 0) {
+                const int p = c0 + b * cpairs + lane;
+                const uint32_t m = cmask[wave][e];
+                const int base = hist[wave][e];
+                const int row = s_off[e] + base + __popc(m & ((1u << tl) - 1u));
+                sorted_pairs[row] = p;
+                pair_rows[p] = row;
+                if ((m >> tl) == 1u) {
+                    hist[wave][e] = base + __popc(m);
+                    cmask[wave][e] = 0u;
+                }
+            }
         }
     }
 }

@@ -113,6 +113,7 @@ def test_route_rejects_pointers(lib):
 def test_forward_rejects(lib):
     assert call_forward(lib, good_dims(tile_m=48)) == L.LILY_ERR_UNSUPPORTED
     assert call_forward(lib, good_dims(H=192)) == L.LILY_ERR_UNSUPPORTED
+    assert call_forward(lib, good_dims(F=192)) == L.LILY_ERR_UNSUPPORTED
     assert call_forward(lib, good_dims(), x=None) == L.LILY_ERR_INVALID_ARG
     assert call_forward(lib, good_dims(), out=FAKE + 2) == L.LILY_ERR_INVALID_ARG
     assert call_forward(lib, good_dims(), ws=None) == L.LILY_ERR_INVALID_ARG
