@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer weight sets cycled")
-    ap.add_argument("--tile-m", type=int, default=64)
+    ap.add_argument("--tile-m", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of layer 0 the CPU oracle computes for the baseline")

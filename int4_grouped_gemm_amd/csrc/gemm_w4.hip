@@ -96,7 +96,6 @@ __device__ __forceinline__ void dequant8(uint32_t v, float s512, float b, uint32
 // is the 16-byte chunk 4h + s of its row.
 constexpr int kGemmThreads = 256;
 constexpr int kGemmWaves = kGemmThreads / kWave;
-constexpr int kNS = 3;  // k-steps in flight through LDS
 constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
 template <bool GATED>
@@ -104,14 +103,26 @@ struct GemmShape {
     static constexpr int BN = GATED ? 128 : 256;  // output columns per workgroup
 };
 
+// Per tile height: k-steps in flight through LDS and workgroups per CU.
+// A single wavefront issues a VALU instruction only every few cycles, so the
+// dequantisation throughput of a SIMD grows with the number of wavefronts it
+// holds: tiles of up to 64 rows keep 4 wavefronts per SIMD (<= 128 VGPRs,
+// <= 40 KB of LDS per workgroup) and double-buffer; 128-row tiles hold 2.
+template <int BM>
+struct Occ {
+    static constexpr int NS = BM >= 128 ? 3 : 2;
+    static constexpr int WAVES_PER_SIMD = BM >= 128 ? 2 : 4;
+};
+
 template <int BM>
 struct Lds {
+    static constexpr int NS = Occ<BM>::NS;
     static constexpr int A = BM * 128;          // bytes of one A stage
     static constexpr int Q = 256 * 32;          // bytes of one weight stage
     static constexpr int SB = 256 * 4 * 2;      // scales, then biases, two k-steps each
     static constexpr int A_OFF = 0;
-    static constexpr int Q_OFF = kNS * A;
-    static constexpr int SB_OFF = Q_OFF + kNS * Q;
+    static constexpr int Q_OFF = NS * A;
+    static constexpr int SB_OFF = Q_OFF + NS * Q;
     static constexpr int TOTAL = SB_OFF + 2 * SB;
 };
 
@@ -161,7 +172,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int 
     const int nk = args.K / 64;
 
     auto issue = [&](int kt) {
-        const int buf = kt % kNS;
+        const int buf = kt % Ld::NS;
         char* a_base = smem + Ld::A_OFF + buf * Ld::A;
 #pragma unroll
         for (int j = 0; j < N_A; ++j)
@@ -186,44 +197,65 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][g][r] = 0.0f;
 
+    constexpr int NS = Ld::NS;
+    static_assert(NS == 2 || NS == 3, "stage count");
     issue(0);
-    if (nk > 1) issue(1);
+    if (NS == 3 && nk > 1) issue(1);
     for (int kt = 0; kt < nk; ++kt) {
-        // Stage kt has landed once only the loads of stage kt + 1 are left.
-        if (kt + 1 >= nk) wait_vmcnt<0>();
+        // Stage kt has landed once only the loads of later stages are left.
+        if (NS == 2 || kt + 1 >= nk) wait_vmcnt<0>();
         else if (kt & 1) wait_vmcnt<N_A + N_Q + N_SB>();  // kt + 1 is even
         else wait_vmcnt<N_A + N_Q>();
         barrier_only();
-        if (kt + 2 < nk) issue(kt + 2);
+        if (kt + NS - 1 < nk) issue(kt + NS - 1);
 
-        const int buf = kt % kNS;
+        const int buf = kt % NS;
         const char* Ab = smem + Ld::A_OFF + buf * Ld::A;
         const char* Qb = smem + Ld::Q_OFF + buf * Ld::Q;
         const char* Sb = smem + Ld::SB_OFF + ((kt >> 1) & 1) * Ld::SB + (kt & 1) * 2;
-        bf16x8 bfr[NI][4];
+        // LDS reads are software-pipelined: the weights and scales of the
+        // step and the A operands of sub-step 0 are requested together, and
+        // the A operands of sub-step s + 1 before the work of sub-step s.
+        u32x4 q[NI];
+        uint16_t sbits[NI], bbits[NI];
 #pragma unroll
         for (int g = 0; g < NI; ++g) {
-            const u32x4 q = *reinterpret_cast<const u32x4*>(Qb + (h * 256 + brow[g]) * 16);
-            const float s512 = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + brow[g] * 4)) * 512.0f;
-            const float b = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + 1024 + brow[g] * 4));
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                uint32_t w[4];
-                dequant8(q[s], s512, b, w);
-                bfr[g][s] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-            }
+            q[g] = *reinterpret_cast<const u32x4*>(Qb + (h * 256 + brow[g]) * 16);
+            sbits[g] = *reinterpret_cast<const uint16_t*>(Sb + brow[g] * 4);
+            bbits[g] = *reinterpret_cast<const uint16_t*>(Sb + 1024 + brow[g] * 4);
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int chunk = 4 * h + s;
+        auto read_a = [&](int s, bf16x8* af) {
 #pragma unroll
             for (int i = 0; i < MIA; ++i) {
                 const int row = 32 * i + lane % 32;
-                const bf16x8 af = *reinterpret_cast<const bf16x8*>(Ab + row * 128 + swz(row, chunk) * 16);
+                af[i] = *reinterpret_cast<const bf16x8*>(Ab + row * 128 + swz(row, 4 * h + s) * 16);
+            }
+        };
+        bf16x8 af_cur[MIA], af_nxt[MIA];
+        read_a(0, af_cur);
+        float s512[NI], bias[NI];
+#pragma unroll
+        for (int g = 0; g < NI; ++g) {
+            s512[g] = bf16_bits_to_float(sbits[g]) * 512.0f;
+            bias[g] = bf16_bits_to_float(bbits[g]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) read_a(s + 1, af_nxt);
+            bf16x8 bfr[NI];
+#pragma unroll
+            for (int g = 0; g < NI; ++g) {
+                uint32_t w[4];
+                dequant8(q[g][s], s512[g], bias[g], w);
+                bfr[g] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            }
+#pragma unroll
+            for (int i = 0; i < MIA; ++i)
 #pragma unroll
                 for (int g = 0; g < NI; ++g)
-                    acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[g][s], acc[i][g], 0, 0, 0);
-            }
+                    acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_cur[i], bfr[g], acc[i][g], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < MIA; ++i) af_cur[i] = af_nxt[i];
         }
         wait_lgkmcnt0();  // this wavefront's LDS reads of the stage are done
     }
@@ -251,7 +283,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int 
 }
 
 template <int BM, bool GATED>
-__global__ void __launch_bounds__(kGemmThreads, 2) moe_w4_gemm(GemmArgs args) {
+__global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_gemm(GemmArgs args) {
     constexpr int BN = GemmShape<GATED>::BN;
     constexpr int MI = BM / 32;
     __shared__ __attribute__((aligned(16))) char smem[Lds<BM>::TOTAL];
