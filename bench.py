@@ -32,7 +32,7 @@ METRIC = "MoE-layer prefill tokens/s (T=2048, int4 g64); % of HBM / MFMA peak"
 WORKLOAD = "prefill2048_zipf"
 PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill2048_zipf.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill2048_zipf.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "int4_grouped_gemm_amd", "csrc", f)
                   for f in ("gemm_w4.hip", "route.hip", "common.hpp")]
 
@@ -160,7 +160,7 @@ def main():
         peak, unit = PEAK_HBM_GBS, "GB/s"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
+        tr = json.loads([ln for ln in open(TRAFFIC_FILE) if ln.startswith("{")][0])
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("stage") == dom \
                 and tr.get("tile_m") == args.tile_m:
             traffic = tr.get("hbm_bytes_per_launch")
