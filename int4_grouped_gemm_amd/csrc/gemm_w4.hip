@@ -114,27 +114,23 @@ struct Occ {
     static constexpr int WAVES_PER_SIMD = BM >= 128 ? 2 : 4;
 };
 
+// LDS layout of a workgroup: per stage, the weights (Q: [2 halves][256
+// rows][16 B]), the scale/bias words (SB: [256 rows] scales then [256 rows]
+// biases, 4 bytes = the aligned pair of groups holding this k-step's) and
+// the A tile ([BM rows][64 bf16]). All stage bases stay below 64 KB so they
+// fit the immediate offset of ds_read.
 template <int BM>
 struct Lds {
     static constexpr int NS = Occ<BM>::NS;
-    static constexpr int A = BM * 128;          // bytes of one A stage
-    static constexpr int Q = 256 * 32;          // bytes of one weight stage
-    static constexpr int SB = 256 * 4 * 2;      // scales, then biases, two k-steps each
-    static constexpr int A_OFF = 0;
-    static constexpr int Q_OFF = NS * A;
+    static constexpr int Q = 256 * 32;
+    static constexpr int SB = 256 * 4 * 2;
+    static constexpr int A = BM * 128;
+    static constexpr int Q_OFF = 0;
     static constexpr int SB_OFF = Q_OFF + NS * Q;
-    static constexpr int TOTAL = SB_OFF + 2 * SB;
+    static constexpr int A_OFF = SB_OFF + NS * SB;
+    static constexpr int TOTAL = A_OFF + NS * A;
+    static_assert(A_OFF + (NS - 1) * A < 65536, "stage bases must fit ds_read offsets");
 };
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One global -> LDS load per lane; lane l lands at lds_wave_base + l * size.
-__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, char* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
-}
 
 // s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
@@ -155,38 +151,59 @@ __device__ __forceinline__ void barrier_only() {
     asm volatile("" ::: "memory");
 }
 
+// Global -> LDS load (gfx950 LDS DMA) with a wave-uniform 64-bit base in
+// SGPRs and a 32-bit per-lane byte offset; lane l lands at LDS address
+// m0 + l * size. The kernel's own code uses M0 for nothing else.
+__device__ __forceinline__ void dma16(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(lane_off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds_addr), "v"(lane_off), "s"(base) : "memory");
+}
+
+// Per-workgroup load plan: for each DMA instruction of this wavefront, a
+// uniform base (advanced per k-step by a fixed stride) and a lane offset.
+template <int MI>
+struct LoadPlan {
+    const char* a_base;      // A rows: + kt * 128
+    uint32_t a_off[MI];      // row byte offset + swizzled chunk
+    const char* q_base[2];   // weight halves: + kt * 32
+    uint32_t q_off[2];
+    const char* sb_base[2];  // scale/bias pairs: + (kt & ~1) * 2
+    uint32_t sb_off[2];
+};
+
 template <int BM, bool GATED, int MIA>
-__device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int r0, int rows,
-                                          const uint16_t* const* a_src, const uint8_t* const* q_src,
-                                          const uint16_t* const* sb_src, const int* brow,
-                                          const int* col0) {
+__device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
+                                          const LoadPlan<BM / 32>& lp, uint32_t wave, int r0,
+                                          int rows, const int* brow, const int* col0) {
     using Ld = Lds<BM>;
+    constexpr int NS = Ld::NS;
     constexpr int NI = 2;
     constexpr int N_A = MIA;  // A loads per wavefront per k-step (8 rows each)
-    constexpr int N_Q = 2;    // weight loads per wavefront per k-step
-    constexpr int N_SB = 2;   // scale/bias loads per wavefront per even k-step
+    constexpr int N_DMA = N_A + 2 + 2;
+    static_assert(NS == 2 || NS == 3, "stage count");
+    const uint32_t smem = (uint32_t)(size_t)smem_p;  // LDS byte address
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = tid / kWave;
     const int h = lane / 32;
     const int nk = args.K / 64;
 
-    auto issue = [&](int kt) {
-        const int buf = kt % Ld::NS;
-        char* a_base = smem + Ld::A_OFF + buf * Ld::A;
+    auto issue = [&](int kt, int buf) {
 #pragma unroll
         for (int j = 0; j < N_A; ++j)
-            dma16(a_src[j] + kt * 64, a_base + (32 * j + 8 * wave) * 128);
-        char* q_base = smem + Ld::Q_OFF + buf * Ld::Q;
+            dma16(lp.a_base + kt * 128, lp.a_off[j],
+                  smem + Ld::A_OFF + buf * Ld::A + (32 * j + 8 * wave) * 128);
 #pragma unroll
-        for (int j = 0; j < N_Q; ++j)
-            dma16(q_src[j] + kt * 32, q_base + 64 * (2 * wave + j) * 16);
-        if ((kt & 1) == 0) {
-            char* sb_base = smem + Ld::SB_OFF + ((kt >> 1) & 1) * Ld::SB;
+        for (int j = 0; j < 2; ++j)
+            dma16(lp.q_base[j] + kt * 32, lp.q_off[j],
+                  smem + Ld::Q_OFF + buf * Ld::Q + 64 * (2 * wave + j) * 16);
 #pragma unroll
-            for (int j = 0; j < N_SB; ++j)
-                dma4(sb_src[j] + kt, sb_base + 64 * (2 * wave + j) * 4);
-        }
+        for (int j = 0; j < 2; ++j)
+            dma4(lp.sb_base[j] + (kt & ~1) * 2, lp.sb_off[j],
+                 smem + Ld::SB_OFF + buf * Ld::SB + 64 * (2 * wave + j) * 4);
     };
 
     f32x16 acc[MIA][NI];
@@ -197,42 +214,44 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][g][r] = 0.0f;
 
-    constexpr int NS = Ld::NS;
-    static_assert(NS == 2 || NS == 3, "stage count");
-    issue(0);
-    if (NS == 3 && nk > 1) issue(1);
-    for (int kt = 0; kt < nk; ++kt) {
-        // Stage kt has landed once only the loads of later stages are left.
-        if (NS == 2 || kt + 1 >= nk) wait_vmcnt<0>();
-        else if (kt & 1) wait_vmcnt<N_A + N_Q + N_SB>();  // kt + 1 is even
-        else wait_vmcnt<N_A + N_Q>();
-        barrier_only();
-        if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    // Per-lane LDS read offsets inside a stage.
+    uint32_t a_rd[MIA][4];
+#pragma unroll
+    for (int i = 0; i < MIA; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int row = 32 * i + lane % 32;
+            a_rd[i][s] = row * 128 + swz(row, 4 * h + s) * 16;
+        }
+    uint32_t q_rd[NI], sb_rd[NI];
+#pragma unroll
+    for (int g = 0; g < NI; ++g) {
+        q_rd[g] = (h * 256 + brow[g]) * 16;
+        sb_rd[g] = brow[g] * 4;
+    }
 
-        const int buf = kt % NS;
-        const char* Ab = smem + Ld::A_OFF + buf * Ld::A;
-        const char* Qb = smem + Ld::Q_OFF + buf * Ld::Q;
-        const char* Sb = smem + Ld::SB_OFF + ((kt >> 1) & 1) * Ld::SB + (kt & 1) * 2;
-        // LDS reads are software-pipelined: the weights and scales of the
-        // step and the A operands of sub-step 0 are requested together, and
-        // the A operands of sub-step s + 1 before the work of sub-step s.
+    // One k-step on stage buffer `buf` (a compile-time constant after the
+    // loop below is unrolled by NS).
+    auto step = [&](int kt, int buf) {
+        if (NS == 2 || kt + 1 >= nk) wait_vmcnt<0>();
+        else wait_vmcnt<N_DMA>();
+        barrier_only();
+        if (kt + NS - 1 < nk) issue(kt + NS - 1, (buf + NS - 1) % NS);
+
+        const char* Ab = smem_p + Ld::A_OFF + buf * Ld::A;
+        const char* Qb = smem_p + Ld::Q_OFF + buf * Ld::Q;
+        const char* Sb = smem_p + Ld::SB_OFF + buf * Ld::SB + (kt & 1) * 2;
         u32x4 q[NI];
         uint16_t sbits[NI], bbits[NI];
 #pragma unroll
         for (int g = 0; g < NI; ++g) {
-            q[g] = *reinterpret_cast<const u32x4*>(Qb + (h * 256 + brow[g]) * 16);
-            sbits[g] = *reinterpret_cast<const uint16_t*>(Sb + brow[g] * 4);
-            bbits[g] = *reinterpret_cast<const uint16_t*>(Sb + 1024 + brow[g] * 4);
+            q[g] = *reinterpret_cast<const u32x4*>(Qb + q_rd[g]);
+            sbits[g] = *reinterpret_cast<const uint16_t*>(Sb + sb_rd[g]);
+            bbits[g] = *reinterpret_cast<const uint16_t*>(Sb + 1024 + sb_rd[g]);
         }
-        auto read_a = [&](int s, bf16x8* af) {
-#pragma unroll
-            for (int i = 0; i < MIA; ++i) {
-                const int row = 32 * i + lane % 32;
-                af[i] = *reinterpret_cast<const bf16x8*>(Ab + row * 128 + swz(row, 4 * h + s) * 16);
-            }
-        };
         bf16x8 af_cur[MIA], af_nxt[MIA];
-        read_a(0, af_cur);
+#pragma unroll
+        for (int i = 0; i < MIA; ++i) af_cur[i] = *reinterpret_cast<const bf16x8*>(Ab + a_rd[i][0]);
         float s512[NI], bias[NI];
 #pragma unroll
         for (int g = 0; g < NI; ++g) {
@@ -241,7 +260,11 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int 
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if (s < 3) read_a(s + 1, af_nxt);
+            if (s < 3) {
+#pragma unroll
+                for (int i = 0; i < MIA; ++i)
+                    af_nxt[i] = *reinterpret_cast<const bf16x8*>(Ab + a_rd[i][s + 1]);
+            }
             bf16x8 bfr[NI];
 #pragma unroll
             for (int g = 0; g < NI; ++g) {
@@ -258,6 +281,14 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem, int 
             for (int i = 0; i < MIA; ++i) af_cur[i] = af_nxt[i];
         }
         wait_lgkmcnt0();  // this wavefront's LDS reads of the stage are done
+    };
+
+    issue(0, 0);
+    if (NS == 3 && nk > 1) issue(1, 1);
+    for (int kt = 0; kt < nk; kt += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u)
+            if (kt + u < nk) step(kt + u, u);
     }
 
     // Epilogue. C layout of a 32x32 tile: lane l, register r holds row
@@ -290,7 +321,7 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = tid / kWave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
     // Tiles are (block, n-tile) pairs: the routed blocks of the block map,
     // then the shared expert's blocks; n-tiles vary fastest. Workgroups are
@@ -324,57 +355,56 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
     const int rows = min(BM, r_end - r0);
     const int K = args.K;
 
+    LoadPlan<MI> lp;
     // A loads: load j of wavefront w fills LDS rows 32j + 8w + lane/8,
     // physical chunk lane%8, which holds logical chunk (lane%8) ^ (row & 7).
     // Rows past the block read the block's first row: their products land in
     // output rows that are never stored.
-    const uint16_t* a_src[MI];
+    lp.a_base = reinterpret_cast<const char*>(args.a);
 #pragma unroll
     for (int j = 0; j < MI; ++j) {
-        const int row = 32 * j + 8 * wave + lane / 8;
+        const int row = 32 * j + 8 * (int)wave + lane / 8;
         const int r = r0 + (row < rows ? row : 0);
         int src_row = r;
         if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
-        a_src[j] = args.a + (size_t)src_row * K + (((lane % 8) ^ (row & 7)) * 8);
+        lp.a_off[j] = (uint32_t)src_row * (uint32_t)(K * 2) + (uint32_t)(((lane % 8) ^ (row & 7)) * 16);
     }
-    // Weight row r_loc (0..255) of the workgroup: matrix and row.
+    // Weight loads. The workgroup's 256 weight rows: gate/up -> rows n0.. of
+    // the gate matrix then the same rows of the up matrix; down -> rows n0..
+    // of W_down. Load j of wavefront w covers 64 consecutive slots
+    // c = 64 (2w + j) + lane: for weights slot (half, row) = (c / 256, c % 256),
+    // for scales c < 256 and biases c >= 256, row c % 256. Each load stays in
+    // one matrix, so its base is uniform.
     const size_t mat = shared ? 0 : (size_t)e * args.N;
-    auto wq = [&](int r_loc) -> const uint8_t* {
-        const int m = GATED ? r_loc / 128 : 0;
-        const int n = GATED ? n0 + r_loc % 128 : n0 + r_loc;
-        return (shared ? args.sq[m] : args.q[m]) + (mat + n) * (K / 2);
-    };
-    auto wsb = [&](int r_loc, bool bias) -> const uint16_t* {
-        const int m = GATED ? r_loc / 128 : 0;
-        const int n = GATED ? n0 + r_loc % 128 : n0 + r_loc;
-        const uint16_t* base = bias ? (shared ? args.sbi[m] : args.bi[m])
-                                    : (shared ? args.ssc[m] : args.sc[m]);
-        return base + (mat + n) * (K / 64);
-    };
-    // Weight loads: load j of wavefront w fills 16-byte slots 64(2w + j) +
-    // lane = (half, row) of the Q stage.
-    const uint8_t* q_src[2];
-    const uint16_t* sb_src[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int ci = 64 * (2 * wave + j) + lane;
-        q_src[j] = wq(ci % 256) + (ci / 256) * 16;
-        sb_src[j] = wsb(ci % 256, ci >= 256);
+        const int c0 = 64 * (2 * (int)wave + j);        // uniform
+        const int r_loc = (c0 % 256) + lane;
+        const int m = GATED ? (c0 % 256) / 128 : 0;      // uniform
+        const int n_in = GATED ? r_loc % 128 : r_loc;    // row inside the workgroup's span
+        const uint8_t* qm = shared ? args.sq[m] : args.q[m];
+        lp.q_base[j] = reinterpret_cast<const char*>(qm + (mat + n0) * (K / 2)) + (c0 / 256) * 16;
+        lp.q_off[j] = (uint32_t)n_in * (uint32_t)(K / 2);
+        const bool is_bias = c0 >= 256;
+        const uint16_t* sm = is_bias ? (shared ? args.sbi[m] : args.bi[m])
+                                     : (shared ? args.ssc[m] : args.sc[m]);
+        lp.sb_base[j] = reinterpret_cast<const char*>(sm + (mat + n0) * (K / 64));
+        lp.sb_off[j] = (uint32_t)n_in * (uint32_t)(K / 64) * 2u;
     }
     int brow[2], col0[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-        brow[g] = GATED ? 128 * g + 32 * wave + lane % 32 : 64 * wave + 32 * g + lane % 32;
-        col0[g] = GATED ? n0 + 32 * wave : n0 + 64 * wave + 32 * g;
+        brow[g] = GATED ? 128 * g + 32 * (int)wave + lane % 32 : 64 * (int)wave + 32 * g + lane % 32;
+        col0[g] = GATED ? n0 + 32 * (int)wave : n0 + 64 * (int)wave + 32 * g;
     }
 
     // Only the 32-row sub-tiles that hold rows of the block are loaded and
     // multiplied.
     const int mia = (rows + 31) / 32;
-    if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
-    else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
-    else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
-    else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, r0, rows, a_src, q_src, sb_src, brow, col0);
+    if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, lp, wave, r0, rows, brow, col0);
+    else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, lp, wave, r0, rows, brow, col0);
+    else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, lp, wave, r0, rows, brow, col0);
+    else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, lp, wave, r0, rows, brow, col0);
 }
 
 // out[t] = bf16(y[P + t] + sum_j w[t, j] * y[pair_rows[t * topk + j]]), fp32,
