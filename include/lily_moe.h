@@ -64,22 +64,40 @@ typedef struct {
 
 /* One groupwise-affine int4 matrix per expert, stacked over n experts
    (n = E for routed, 1 for the shared expert), for a matrix of N rows
-   (outputs) and K columns (inputs):
+   (outputs) and K columns (inputs), in the plain layout:
      q:     uint8 [n, N, K/2]; byte i of a row = element 2i (low nibble)
             and element 2i+1 (high nibble), values 0..15;
      scale: bf16 bits [n, N, K/64];
      bias:  bf16 bits [n, N, K/64];
-   weight (e, row, col) = bf16(scale[e,row,col/64] * q + bias[e,row,col/64]). */
+   weight (e, row, col) = bf16(scale[e,row,col/64] * q + bias[e,row,col/64]).
+   lily_w4_pack converts this layout into the packed one the GEMMs read. */
 typedef struct {
     const uint8_t* q;
     const uint16_t* scale;
     const uint16_t* bias;
 } lily_w4;
 
-/* gate, up: N = F, K = H.  down: N = H, K = F. */
+/* Packed layout of the same matrix stack (N a multiple of 128, K a
+   multiple of 64): one 4608-byte block per (expert e, 128-row slab s, group
+   g), block index (e * N/128 + s) * K/64 + g; inside a block, for slab row
+   r = 0..127 (matrix row 128 s + r) and half h = 0, 1:
+     bytes 16 (128 h + r) .. +15:  q bytes 32 g + 16 h .. +15 of the row
+                                   (elements 64 g + 32 h .. +31);
+     bytes 4096 + 2 r:             scale of (row, group g);
+     bytes 4352 + 2 r:             bias of (row, group g).
+   Same size as the plain layout: n * N * K * 9 / 16 bytes. A workgroup's
+   weights for one k-step are two contiguous 4 KB runs plus 512-byte scale
+   and bias runs, so every load is a full, coalesced line. */
+
+/* gate, up: N = F, K = H.  down: N = H, K = F. Each pointer is a packed
+   matrix stack (16-byte aligned) written by lily_w4_pack. */
 typedef struct {
-    lily_w4 gate, up, down;          /* routed experts, n = E */
-    lily_w4 sh_gate, sh_up, sh_down; /* shared expert, n = 1 */
+    const void* gate;
+    const void* up;
+    const void* down;     /* routed experts, n = E */
+    const void* sh_gate;
+    const void* sh_up;
+    const void* sh_down;  /* shared expert, n = 1 */
 } lily_moe_weights;
 
 /* Outputs of lily_moe_route (inputs of lily_moe_forward). P = T * topk.
@@ -96,7 +114,20 @@ typedef struct {
                               min(block_row0[b] + tile_m, offsets[e+1]) - 1 of
                               expert e = block_expert[b]; experts ascending;
                               entries at and past num_blocks are unspecified;
-   num_blocks int32 [1]       number of valid blocks (stays on the device). */
+   num_blocks int32 [1]       number of valid blocks (stays on the device);
+   block_order int32 [lily_moe_max_blocks(dims)]
+                              schedule of the grouped GEMMs (not part of the
+                              method's result): the full blocks (tile_m
+                              rows) in block order, then each expert's last,
+                              partial block by descending size class
+                              ceil(4 rows / tile_m), ties in expert order;
+   sched int32 [LILY_SCHED_INTS]
+                              work-queue counters of the grouped GEMMs. Zero
+                              them once after allocating; lily_moe_route
+                              clears them and every GEMM launch leaves them
+                              zero when it completes. Launches that share a
+                              routing buffer must be ordered on one stream. */
+#define LILY_SCHED_INTS 32
 typedef struct {
     int32_t* topk_ids;
     float* topk_w;
@@ -107,6 +138,8 @@ typedef struct {
     int32_t* block_expert;
     int32_t* block_row0;
     int32_t* num_blocks;
+    int32_t* block_order;
+    int32_t* sched;
 } lily_moe_routing;
 
 /* Host, pure. Capacity of the block map: ceil(P / tile_m) + min(E, P).
@@ -118,6 +151,19 @@ int32_t lily_moe_max_blocks(const lily_moe_dims* dims);
    and the per-row expert outputs y (fp32) for the P routed rows and the T
    shared rows. */
 size_t lily_moe_workspace_bytes(const lily_moe_dims* dims);
+
+/* Host, pure. Bytes of the packed layout of an n-expert stack of [N, K]
+   matrices (0 if N is not a multiple of 128, K not a multiple of 64, group
+   not 64, or a size is < 1). */
+size_t lily_w4_packed_bytes(int32_t n, int32_t N, int32_t K, int32_t group);
+
+/* Rearranges a plain-layout matrix stack into the packed layout (a pure
+   permutation of bytes: no value changes). packed: lily_w4_packed_bytes
+   bytes of device memory, not overlapping the inputs. Errors:
+   LILY_ERR_INVALID_ARG (null or misaligned pointer, bad sizes),
+   LILY_ERR_HIP. */
+int lily_w4_pack(const lily_w4* w, int32_t n, int32_t N, int32_t K, int32_t group, void* packed,
+                 void* stream);
 
 /* Routing of one MoE layer: top-k and softmax per token, histogram,
    exclusive scan, stable scatter and block map, all enqueued on `stream`

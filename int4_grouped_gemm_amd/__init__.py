@@ -23,9 +23,11 @@ LILY_ERR_UNSUPPORTED = -2
 LILY_ERR_WORKSPACE = -3
 LILY_ERR_HIP = -4
 
-EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_moe_route",
-           "lily_moe_forward", "lily_moe_gate_up", "lily_moe_down", "lily_moe_combine",
-           "lily_residual_norm", "lily_last_error")
+EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
+           "lily_w4_pack", "lily_moe_route", "lily_moe_forward", "lily_moe_gate_up",
+           "lily_moe_down", "lily_moe_combine", "lily_residual_norm", "lily_last_error")
+LILY_SCHED_INTS = 32
+WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
 
 class LilyMoeDims(ctypes.Structure):
@@ -39,11 +41,12 @@ class LilyW4(ctypes.Structure):
 
 
 class LilyMoeWeights(ctypes.Structure):
-    _fields_ = [(n, LilyW4) for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")]
+    """Packed weight stacks (device pointers written by lily_w4_pack)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
 
 
 ROUTING_FIELDS = ("topk_ids", "topk_w", "counts", "offsets", "sorted_pairs", "pair_rows",
-                  "block_expert", "block_row0", "num_blocks")
+                  "block_expert", "block_row0", "num_blocks", "block_order", "sched")
 
 
 class LilyMoeRouting(ctypes.Structure):
@@ -74,6 +77,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_moe_max_blocks.argtypes = [P(LilyMoeDims)]
     lib.lily_moe_workspace_bytes.restype = ctypes.c_size_t
     lib.lily_moe_workspace_bytes.argtypes = [P(LilyMoeDims)]
+    lib.lily_w4_packed_bytes.restype = ctypes.c_size_t
+    lib.lily_w4_packed_bytes.argtypes = [ctypes.c_int32] * 4
+    lib.lily_w4_pack.restype = ctypes.c_int
+    lib.lily_w4_pack.argtypes = [P(LilyW4), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.lily_moe_route.restype = ctypes.c_int
     lib.lily_moe_route.argtypes = [P(LilyMoeDims), ctypes.c_void_p, P(LilyMoeRouting),
                                    ctypes.c_void_p]
@@ -131,7 +139,8 @@ def _check(rc: int, lib: ctypes.CDLL) -> None:
 
 @dataclasses.dataclass
 class W4:
-    """One stacked int4 matrix set on the device (uint8 q, int16 bf16 bits)."""
+    """One stacked int4 matrix set on the device in the plain layout (uint8 q,
+    int16 bf16 bits); the input of lily_w4_pack."""
 
     q: torch.Tensor
     scale: torch.Tensor
@@ -143,18 +152,19 @@ class W4:
 
 @dataclasses.dataclass
 class Weights:
-    gate: W4
-    up: W4
-    down: W4
-    sh_gate: W4
-    sh_up: W4
-    sh_down: W4
+    """The six packed matrix stacks of one layer (uint8 device tensors)."""
+
+    gate: torch.Tensor
+    up: torch.Tensor
+    down: torch.Tensor
+    sh_gate: torch.Tensor
+    sh_up: torch.Tensor
+    sh_down: torch.Tensor
 
     def c(self) -> LilyMoeWeights:
         # device pointers do not change while the tensors live: build once
         if getattr(self, "_c", None) is None:
-            self._c = LilyMoeWeights(*(getattr(self, n).c() for n in
-                                       ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")))
+            self._c = LilyMoeWeights(*(_ptr(getattr(self, n)) for n in WEIGHT_FIELDS))
         return self._c
 
 
@@ -169,6 +179,8 @@ class Routing:
     block_expert: torch.Tensor
     block_row0: torch.Tensor
     num_blocks: torch.Tensor
+    block_order: torch.Tensor
+    sched: torch.Tensor
 
     def c(self) -> LilyMoeRouting:
         if getattr(self, "_c", None) is None:
@@ -189,6 +201,20 @@ def lily_moe_workspace_bytes(d: LilyMoeDims) -> int:
     if n == 0:
         raise LilyError(LILY_ERR_INVALID_ARG, lib.lily_last_error().decode())
     return n
+
+
+def lily_w4_packed_bytes(n: int, N: int, K: int, group: int = 64) -> int:
+    lib = load()
+    b = lib.lily_w4_packed_bytes(n, N, K, group)
+    if b == 0:
+        raise LilyError(LILY_ERR_INVALID_ARG, lib.lily_last_error().decode())
+    return b
+
+
+def lily_w4_pack(w: W4, n: int, N: int, K: int, packed, group: int = 64, stream=None) -> None:
+    lib = load()
+    rc = lib.lily_w4_pack(ctypes.byref(w.c()), n, N, K, group, _ptr(packed), _stream(stream))
+    _check(rc, lib)
 
 
 def lily_moe_route(d: LilyMoeDims, logits, routing: Routing, stream=None) -> None:
@@ -254,7 +280,8 @@ def alloc_routing(d: LilyMoeDims, device="cuda") -> Routing:
                    counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
                    sorted_pairs=torch.empty(P, **i32), pair_rows=torch.empty(P, **i32),
                    block_expert=torch.empty(mb, **i32), block_row0=torch.empty(mb, **i32),
-                   num_blocks=torch.empty(1, **i32))
+                   num_blocks=torch.empty(1, **i32), block_order=torch.empty(mb, **i32),
+                   sched=torch.zeros(LILY_SCHED_INTS, **i32))
 
 
 def alloc_workspace(d: LilyMoeDims, device="cuda") -> torch.Tensor:
@@ -273,11 +300,24 @@ def workspace_views(d: LilyMoeDims, ws: torch.Tensor):
     return h, y
 
 
+def pack_w4(w: W4, n: int, N: int, K: int, stream=None) -> torch.Tensor:
+    """Packed copy (uint8 device tensor) of a plain-layout matrix stack."""
+    out = torch.empty(lily_w4_packed_bytes(n, N, K), dtype=torch.uint8, device=w.q.device)
+    lily_w4_pack(w, n, N, K, out, stream=stream)
+    return out
+
+
 def weights_from_host(lw, device="cuda") -> Weights:
-    """Upload a ``synth.LayerWeights`` (numpy, canonical layout) to the device."""
-    def up(w) -> W4:
-        return W4(torch.from_numpy(w.q).to(device),
-                  torch.from_numpy(w.scale.view("int16")).to(device),
-                  torch.from_numpy(w.bias.view("int16")).to(device))
-    return Weights(up(lw.gate), up(lw.up), up(lw.down), up(lw.sh_gate), up(lw.sh_up),
-                   up(lw.sh_down))
+    """Upload a ``synth.LayerWeights`` (numpy, plain layout) and pack it on the
+    device; the plain copies are freed once packed."""
+    packed = {}
+    for name in WEIGHT_FIELDS:
+        m = getattr(lw, name)
+        n, N, K2 = m.q.shape
+        plain = W4(torch.from_numpy(m.q).to(device),
+                   torch.from_numpy(m.scale.view("int16")).to(device),
+                   torch.from_numpy(m.bias.view("int16")).to(device))
+        packed[name] = pack_w4(plain, n, N, 2 * K2)
+        torch.cuda.current_stream(packed[name].device).synchronize()
+        del plain
+    return Weights(**packed)

@@ -32,6 +32,8 @@ int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_
 int launch_combine(const lily_moe_dims& d, const float* y, const lily_moe_routing& r,
                    uint16_t* out, hipStream_t stream);
 size_t forward_workspace_bytes(const lily_moe_dims& d);
+size_t packed_w4_bytes(int n, int N, int K);
+int launch_pack(const lily_w4& w, int n, int N, int K, void* packed, hipStream_t stream);
 void forward_workspace_split(const lily_moe_dims& d, void* ws, uint16_t** h, float** y);
 int launch_residual_norm(int T, int H, float* r, const uint16_t* out, uint16_t* x_next,
                          float eps, hipStream_t stream);
@@ -83,14 +85,26 @@ static int check_routing(const lily_moe_routing* r) {
     REQUIRE_PTR(r->block_expert);
     REQUIRE_PTR(r->block_row0);
     REQUIRE_PTR(r->num_blocks);
+    REQUIRE_PTR(r->block_order);
+    REQUIRE_PTR(r->sched);
     return LILY_OK;
 }
 
-static int check_w4(const lily_w4& w, const char* name) {
-    if (!w.q || !w.scale || !w.bias)
-        return set_error(LILY_ERR_INVALID_ARG, "weights.%s has a NULL pointer", name);
-    if (!aligned16(w.q) || !aligned16(w.scale) || !aligned16(w.bias))
-        return set_error(LILY_ERR_INVALID_ARG, "weights.%s is not 16-byte aligned", name);
+static int check_packed(const void* p, const char* name) {
+    if (!p) return set_error(LILY_ERR_INVALID_ARG, "weights.%s is NULL", name);
+    if (!aligned16(p)) return set_error(LILY_ERR_INVALID_ARG, "weights.%s is not 16-byte aligned", name);
+    return LILY_OK;
+}
+
+static int check_pack_sizes(int32_t n, int32_t N, int32_t K, int32_t group) {
+    if (n < 1 || N < 1 || K < 1)
+        return set_error(LILY_ERR_INVALID_ARG, "n = %d, N = %d, K = %d must be >= 1", n, N, K);
+    if (group != kGroup)
+        return set_error(LILY_ERR_INVALID_ARG, "group = %d; only 64 is supported", group);
+    if (N % 128) return set_error(LILY_ERR_INVALID_ARG, "N = %d is not a multiple of 128", N);
+    if (K % kGroup) return set_error(LILY_ERR_INVALID_ARG, "K = %d is not a multiple of 64", K);
+    if ((int64_t)n * N * K > ((int64_t)1 << 40))
+        return set_error(LILY_ERR_INVALID_ARG, "n * N * K too large");
     return LILY_OK;
 }
 
@@ -99,9 +113,11 @@ static int check_forward_args(const lily_moe_dims* dims, const lily_moe_weights*
     int rc = check_dims(dims);
     if (rc) return rc;
     if (!weights) return set_error(LILY_ERR_INVALID_ARG, "weights is NULL");
-    if ((rc = check_w4(weights->gate, "gate")) || (rc = check_w4(weights->up, "up")) ||
-        (rc = check_w4(weights->down, "down")) || (rc = check_w4(weights->sh_gate, "sh_gate")) ||
-        (rc = check_w4(weights->sh_up, "sh_up")) || (rc = check_w4(weights->sh_down, "sh_down")))
+    if ((rc = check_packed(weights->gate, "gate")) || (rc = check_packed(weights->up, "up")) ||
+        (rc = check_packed(weights->down, "down")) ||
+        (rc = check_packed(weights->sh_gate, "sh_gate")) ||
+        (rc = check_packed(weights->sh_up, "sh_up")) ||
+        (rc = check_packed(weights->sh_down, "sh_down")))
         return rc;
     rc = check_routing(routing);
     if (rc) return rc;
@@ -130,6 +146,23 @@ int32_t lily_moe_max_blocks(const lily_moe_dims* dims) {
 size_t lily_moe_workspace_bytes(const lily_moe_dims* dims) {
     if (check_dims(dims)) return 0;
     return forward_workspace_bytes(*dims);
+}
+
+size_t lily_w4_packed_bytes(int32_t n, int32_t N, int32_t K, int32_t group) {
+    if (check_pack_sizes(n, N, K, group)) return 0;
+    return packed_w4_bytes(n, N, K);
+}
+
+int lily_w4_pack(const lily_w4* w, int32_t n, int32_t N, int32_t K, int32_t group, void* packed,
+                 void* stream) {
+    int rc = check_pack_sizes(n, N, K, group);
+    if (rc) return rc;
+    if (!w) return set_error(LILY_ERR_INVALID_ARG, "w is NULL");
+    REQUIRE_PTR(w->q);
+    REQUIRE_PTR(w->scale);
+    REQUIRE_PTR(w->bias);
+    REQUIRE_PTR(packed);
+    return launch_pack(*w, n, N, K, packed, reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_moe_route(const lily_moe_dims* dims, const float* logits,

@@ -12,6 +12,7 @@ constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kGroup = 64;     // weights per (scale, bias) group
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 64;
+constexpr int kSchedInts = LILY_SCHED_INTS;  // GEMM work-queue counters in a routing
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

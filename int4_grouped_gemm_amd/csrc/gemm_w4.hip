@@ -7,46 +7,60 @@
 // section "Prefill"). Here the on-chip memory is the LDS of a CDNA4 compute
 // unit and the products run on bf16 MFMA (v_mfma_f32_32x32x16_bf16).
 //
-// One workgroup computes one (block, n-tile) of one expert:
+// A tile is one (block, n-tile) pair of one expert:
 //   rows  = a block of the block map (or of the shared expert's T rows);
 //   cols  = BN outputs of the expert's weight matrix (for the gate/up GEMM,
 //           BN columns of both gate and up, so that SwiGLU can be applied
 //           in the epilogue).
 // K runs in steps of 64 = one quantisation group per weight row, so each
-// step needs one scale and one bias per row. Global loads of step s+1 are
-// issued before the MFMAs of step s (register prefetch); dequantisation
-// happens when the prefetched nibbles are written to LDS.
+// step needs one scale and one bias per row. Operands move global -> LDS by
+// DMA a few steps ahead of use; each wavefront dequantises its own weights
+// from LDS straight into MFMA operand registers. The weights are read in
+// the packed layout of lily_w4_pack: the 128 rows x 64 k of a slab and
+// group, with their scales and biases, are one contiguous 4608-byte block.
 //
-// LDS tiles are [rows][64] bf16 with the 16-byte chunks of each row
-// XOR-swizzled by (row & 7), so that 32 lanes reading one chunk column of
-// 32 consecutive rows hit distinct banks.
+// The grid is persistent (as many workgroups as fit on the device) and
+// takes tiles from eight work queues, one per XCD: queue x owns the blocks
+// x, x + 8, ... of the schedule (the shared expert's blocks, then the
+// routed blocks in block_order, largest first), with their n-tiles
+// consecutive so that they meet the same A rows in one L2.
+//
+// LDS A tiles are [rows][64] bf16 with the 16-byte chunks of each row
+// XOR-swizzled by ((row >> 1) & 7). The LDS has 64 four-byte banks, so a
+// 16-lane phase of a 16-byte read covers 256 bytes: rows r and r + 1 of one
+// chunk column already fall in different halves of the banks, and the
+// swizzle spreads each half's eight rows over its eight chunk slots.
 #include "common.hpp"
 
 namespace lily {
+
+// Packed weight layout (lily_w4_pack): one block per (expert, 128-row slab,
+// group of 64 k); q as [2 halves][128 rows][16 bytes], then the 128 scales,
+// then the 128 biases.
+constexpr int kPackRows = 128;
+constexpr int kPackQ = 4096;
+constexpr int kPackBlock = 4608;
 
 struct GemmArgs {
     const uint16_t* a;              // A rows: gate/up -> x [T, K]; down -> h [P + T, K]
     const int32_t* sorted_pairs;    // gate/up: routed row r reads x[sorted_pairs[r] / topk]
     int topk;
-    const uint8_t* q[2];            // routed weights [E, N, K/2] (gate/up: [0]=gate, [1]=up)
-    const uint16_t* sc[2];          // [E, N, K/64]
-    const uint16_t* bi[2];
-    const uint8_t* sq[2];           // shared expert weights [1, N, K/2]
-    const uint16_t* ssc[2];
-    const uint16_t* sbi[2];
+    const char* w[2];               // packed routed stacks: gate/up -> gate, up; down -> W_down twice
+    const char* sw[2];              // packed shared-expert stacks, same roles
     int N, K;
     const int32_t* block_expert;
     const int32_t* block_row0;
+    const int32_t* block_order;
     const int32_t* num_blocks;
     const int32_t* offsets;
-    int max_blocks;
     int shared_blocks;  // ceil(T / BM)
     int P, T;
-    uint16_t* h_out;  // gate/up: h [P + T, N] bf16
-    float* y_out;     // down: y [P + T, N] fp32
+    int32_t* sched;     // kXcds queue counters, then the finished-workgroup counter
+    uint16_t* h_out;    // gate/up: h [P + T, N] bf16
+    float* y_out;       // down: y [P + T, N] fp32
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (a few ulp
 // of fp32, far below the bf16 rounding of h that follows).
@@ -76,17 +90,17 @@ __device__ __forceinline__ void dequant8(uint32_t v, float s512, float b, uint32
 
 // Tile geometry. A workgroup has 4 wavefronts that split the output columns;
 // every wavefront covers all BM rows of the block. The workgroup owns 256
-// weight rows: for the gate/up GEMM 128 gate rows and the same 128 up rows
-// (so SwiGLU is local to a lane), for the down GEMM 256 rows of W_down.
+// weight rows, two packed slabs: for the gate/up GEMM slab n-tile of the
+// gate matrix and the same slab of the up matrix (so SwiGLU is local to a
+// lane), for the down GEMM slabs 2 n-tile and 2 n-tile + 1 of W_down.
 // Wavefront w takes two groups of 32 weight rows: gate/up -> gate rows
 // 32w.. and up rows 128+32w..; down -> rows 64w.. and 64w+32...
 //
 // Every operand travels global -> LDS with global_load_lds (no registers,
-// no compiler-managed waits), kNS k-steps in flight:
-//   A stage  [BM rows][64 bf16], 16-byte chunks XOR-swizzled by (row & 7);
-//   Q stage  [2 halves][256 rows][16 bytes] of int4 weights;
-//   SB ring  scales then biases of the 256 rows for two k-steps (4 bytes a
-//            row), refreshed every other k-step.
+// no compiler-managed waits), NS k-steps in flight:
+//   A stage  [BM rows][64 bf16], 16-byte chunks XOR-swizzled (swz);
+//   Q stage  [2 halves][256 rows][16 B] of int4 weights;
+//   SB stage the 256 scales, then the 256 biases of the step's group.
 // Each lane then dequantises its own 32 weights of a k-step from LDS into
 // MFMA operand registers (no weight is dequantised twice in a workgroup).
 //
@@ -95,7 +109,6 @@ __device__ __forceinline__ void dequant8(uint32_t v, float s512, float b, uint32
 // 8s..8s+7 of each half, for A and B alike. So a lane's A operand for step s
 // is the 16-byte chunk 4h + s of its row.
 constexpr int kGemmThreads = 256;
-constexpr int kGemmWaves = kGemmThreads / kWave;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
 template <bool GATED>
@@ -103,27 +116,25 @@ struct GemmShape {
     static constexpr int BN = GATED ? 128 : 256;  // output columns per workgroup
 };
 
-// Per tile height: k-steps in flight through LDS and workgroups per CU.
+// Per tile height: k-steps in flight through LDS and wavefronts per SIMD.
 // A single wavefront issues a VALU instruction only every few cycles, so the
 // dequantisation throughput of a SIMD grows with the number of wavefronts it
-// holds: tiles of up to 64 rows keep 4 wavefronts per SIMD (<= 128 VGPRs,
-// <= 40 KB of LDS per workgroup) and double-buffer; 128-row tiles hold 2.
+// holds; 128-row tiles need ~250 VGPRs and hold 2.
 template <int BM>
 struct Occ {
     static constexpr int NS = BM >= 128 ? 3 : 2;
-    static constexpr int WAVES_PER_SIMD = BM >= 128 ? 2 : 4;
+    static constexpr int WAVES_PER_SIMD = BM >= 128 ? 2 : (BM == 64 ? 3 : 4);
 };
 
-// LDS layout of a workgroup: per stage, the weights (Q: [2 halves][256
-// rows][16 B]), the scale/bias words (SB: [256 rows] scales then [256 rows]
-// biases, 4 bytes = the aligned pair of groups holding this k-step's) and
+// LDS layout of a workgroup, per stage: the weights (Q: [2 halves][256
+// rows][16 B]), the scales and biases (SB: [256] bf16 then [256] bf16) and
 // the A tile ([BM rows][64 bf16]). All stage bases stay below 64 KB so they
 // fit the immediate offset of ds_read.
 template <int BM>
 struct Lds {
     static constexpr int NS = Occ<BM>::NS;
     static constexpr int Q = 256 * 32;
-    static constexpr int SB = 256 * 4 * 2;
+    static constexpr int SB = 256 * 2 * 2;
     static constexpr int A = BM * 128;
     static constexpr int Q_OFF = 0;
     static constexpr int SB_OFF = Q_OFF + NS * Q;
@@ -163,47 +174,60 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t lane_off, uint32
                  :: "s"(lds_addr), "v"(lane_off), "s"(base) : "memory");
 }
 
-// Per-workgroup load plan: for each DMA instruction of this wavefront, a
-// uniform base (advanced per k-step by a fixed stride) and a lane offset.
+// Next item of a work queue, the same value in every thread of the
+// workgroup. The first barrier keeps the slot from being overwritten while
+// a wavefront still reads the previous value.
+__device__ __forceinline__ int grab(int32_t* ctr, int* s_next) {
+    __syncthreads();
+    if (threadIdx.x == 0) *s_next = atomicAdd(ctr, 1);
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_next);
+}
+
+// Per-tile load plan of one wavefront: the A row offsets of its DMA loads
+// and the packed block of its weight slab at k-step 0 (+ kt * kPackBlock).
 template <int MI>
 struct LoadPlan {
     const char* a_base;      // A rows: + kt * 128
     uint32_t a_off[MI];      // row byte offset + swizzled chunk
-    const char* q_base[2];   // weight halves: + kt * 32
-    uint32_t q_off[2];
-    const char* sb_base[2];  // scale/bias pairs: + (kt & ~1) * 2
-    uint32_t sb_off[2];
+    const char* w_base;
 };
 
+// Loads, multiplies and stores one tile; returns the workgroup's next queue
+// item, taken after the k-loop so that its latency overlaps the stores.
 template <int BM, bool GATED, int MIA>
-__device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
-                                          const LoadPlan<BM / 32>& lp, uint32_t wave, int r0,
-                                          int rows, const int* brow, const int* col0) {
+__device__ __forceinline__ int gemm_main(const GemmArgs& args, char* smem_p,
+                                         const LoadPlan<BM / 32>& lp, uint32_t wave, int r0,
+                                         int rows, const int* brow, const int* col0,
+                                         int32_t* ctr, int* s_next) {
     using Ld = Lds<BM>;
     constexpr int NS = Ld::NS;
     constexpr int NI = 2;
     constexpr int N_A = MIA;  // A loads per wavefront per k-step (8 rows each)
-    constexpr int N_DMA = N_A + 2 + 2;
+    constexpr int N_DMA = N_A + 3;
     static_assert(NS == 2 || NS == 3, "stage count");
     const uint32_t smem = (uint32_t)(size_t)smem_p;  // LDS byte address
-    const int tid = threadIdx.x;
-    const int lane = tid % kWave;
+    const int lane = threadIdx.x % kWave;
     const int h = lane / 32;
     const int nk = args.K / 64;
+
+    // Weight DMA of this wavefront: half wh of slab wb, rows 0-63 and 64-127
+    // (1 KB each), and the 128 scales (wh = 0) or biases (wh = 1).
+    const uint32_t wh = wave & 1u, wb = wave >> 1;
+    const uint32_t q_off = (wh * 128u + (uint32_t)lane) * 16u;
+    const uint32_t sb_off = (uint32_t)kPackQ + wh * 256u + (uint32_t)lane * 4u;
+    const uint32_t q_lds = smem + Ld::Q_OFF + (wh * 256u + wb * 128u) * 16u;
+    const uint32_t sb_lds = smem + Ld::SB_OFF + wh * 512u + wb * 256u;
 
     auto issue = [&](int kt, int buf) {
 #pragma unroll
         for (int j = 0; j < N_A; ++j)
             dma16(lp.a_base + kt * 128, lp.a_off[j],
                   smem + Ld::A_OFF + buf * Ld::A + (32 * j + 8 * wave) * 128);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            dma16(lp.q_base[j] + kt * 32, lp.q_off[j],
-                  smem + Ld::Q_OFF + buf * Ld::Q + 64 * (2 * wave + j) * 16);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            dma4(lp.sb_base[j] + (kt & ~1) * 2, lp.sb_off[j],
-                 smem + Ld::SB_OFF + buf * Ld::SB + 64 * (2 * wave + j) * 4);
+        const char* blk = lp.w_base + (size_t)kt * kPackBlock;
+        dma16(blk, q_off, q_lds + buf * Ld::Q);
+        dma16(blk, q_off + 64 * 16, q_lds + buf * Ld::Q + 64 * 16);
+        dma4(blk, sb_off, sb_lds + buf * Ld::SB);
     };
 
     f32x16 acc[MIA][NI];
@@ -214,20 +238,19 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][g][r] = 0.0f;
 
-    // Per-lane LDS read offsets inside a stage.
-    uint32_t a_rd[MIA][4];
+    // Per-lane LDS read offsets inside a stage. The swizzle depends on row
+    // bits 1-3 only, so the 32-row sub-tiles i differ by a constant i * 4096.
+    uint32_t a_rd[4];
 #pragma unroll
-    for (int i = 0; i < MIA; ++i)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int row = 32 * i + lane % 32;
-            a_rd[i][s] = row * 128 + swz(row, 4 * h + s) * 16;
-        }
+    for (int s = 0; s < 4; ++s) {
+        const int row = lane % 32;
+        a_rd[s] = row * 128 + swz(row, 4 * h + s) * 16;
+    }
     uint32_t q_rd[NI], sb_rd[NI];
 #pragma unroll
     for (int g = 0; g < NI; ++g) {
         q_rd[g] = (h * 256 + brow[g]) * 16;
-        sb_rd[g] = brow[g] * 4;
+        sb_rd[g] = brow[g] * 2;
     }
 
     // One k-step on stage buffer `buf` (a compile-time constant after the
@@ -240,45 +263,68 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
 
         const char* Ab = smem_p + Ld::A_OFF + buf * Ld::A;
         const char* Qb = smem_p + Ld::Q_OFF + buf * Ld::Q;
-        const char* Sb = smem_p + Ld::SB_OFF + buf * Ld::SB + (kt & 1) * 2;
+        const char* Sb = smem_p + Ld::SB_OFF + buf * Ld::SB;
+        // The weights' LDS reads are issued first and each sub-step's A
+        // fragments one sub-step ahead; the MFMAs of sub-step s run while
+        // the weights of sub-step s + 1 are dequantised.
         u32x4 q[NI];
         uint16_t sbits[NI], bbits[NI];
 #pragma unroll
         for (int g = 0; g < NI; ++g) {
             q[g] = *reinterpret_cast<const u32x4*>(Qb + q_rd[g]);
             sbits[g] = *reinterpret_cast<const uint16_t*>(Sb + sb_rd[g]);
-            bbits[g] = *reinterpret_cast<const uint16_t*>(Sb + 1024 + sb_rd[g]);
+            bbits[g] = *reinterpret_cast<const uint16_t*>(Sb + 512 + sb_rd[g]);
         }
-        bf16x8 af_cur[MIA], af_nxt[MIA];
+        bf16x8 af[2][MIA];
 #pragma unroll
-        for (int i = 0; i < MIA; ++i) af_cur[i] = *reinterpret_cast<const bf16x8*>(Ab + a_rd[i][0]);
+        for (int i = 0; i < MIA; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(Ab + i * 4096 + a_rd[0]);
         float s512[NI], bias[NI];
 #pragma unroll
         for (int g = 0; g < NI; ++g) {
             s512[g] = bf16_bits_to_float(sbits[g]) * 512.0f;
             bias[g] = bf16_bits_to_float(bbits[g]);
         }
+        bf16x8 bfr[2][NI];
+        auto dq = [&](int s, bf16x8* dst) {
+#pragma unroll
+            for (int g = 0; g < NI; ++g) {
+                uint32_t w[4];
+                dequant8(q[g][s], s512[g], bias[g], w);
+                dst[g] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            }
+        };
+        dq(0, bfr[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s < 3) {
 #pragma unroll
                 for (int i = 0; i < MIA; ++i)
-                    af_nxt[i] = *reinterpret_cast<const bf16x8*>(Ab + a_rd[i][s + 1]);
-            }
-            bf16x8 bfr[NI];
-#pragma unroll
-            for (int g = 0; g < NI; ++g) {
-                uint32_t w[4];
-                dequant8(q[g][s], s512[g], bias[g], w);
-                bfr[g] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+                    af[(s + 1) & 1][i] = *reinterpret_cast<const bf16x8*>(Ab + i * 4096 + a_rd[s + 1]);
+                dq(s + 1, bfr[(s + 1) & 1]);
             }
 #pragma unroll
             for (int i = 0; i < MIA; ++i)
 #pragma unroll
                 for (int g = 0; g < NI; ++g)
-                    acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_cur[i], bfr[g], acc[i][g], 0, 0, 0);
+                    acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][g], acc[i][g], 0, 0, 0);
+        }
+        // Issue order for the scheduler: the weights' reads and sub-step 0's
+        // A reads, the scale/bias conversion and sub-step 0's dequantisation;
+        // then per sub-step the next A reads and each MFMA followed by a
+        // share of the next sub-step's dequantisation.
+        constexpr int kMfmaPerSub = MIA * NI;
+        constexpr int kDqValu = 19 * NI;
+        constexpr int kValuPerMfma = (kDqValu + kMfmaPerSub - 1) / kMfmaPerSub;
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 * NI + MIA, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * NI + kDqValu, 0);
 #pragma unroll
-            for (int i = 0; i < MIA; ++i) af_cur[i] = af_nxt[i];
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, MIA, 0);
+#pragma unroll
+            for (int m = 0; m < kMfmaPerSub; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (s < 3) __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+            }
         }
         wait_lgkmcnt0();  // this wavefront's LDS reads of the stage are done
     };
@@ -290,6 +336,8 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         for (int u = 0; u < NS; ++u)
             if (kt + u < nk) step(kt + u, u);
     }
+
+    const int next = grab(ctr, s_next);
 
     // Epilogue. C layout of a 32x32 tile: lane l, register r holds row
     // 8*(r/4) + 4*(l/32) + r%4 and column l%32.
@@ -311,6 +359,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
             }
         }
     }
+    return next;
 }
 
 template <int BM, bool GATED>
@@ -318,93 +367,111 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
     constexpr int BN = GemmShape<GATED>::BN;
     constexpr int MI = BM / 32;
     __shared__ __attribute__((aligned(16))) char smem[Lds<BM>::TOTAL];
+    __shared__ int s_next;
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-    // Tiles are (block, n-tile) pairs: the routed blocks of the block map,
-    // then the shared expert's blocks; n-tiles vary fastest. Workgroups are
-    // dispatched to the 8 XCDs round-robin, so workgroup L runs on XCD L % 8;
-    // each XCD takes a contiguous range of the live tiles, so that the
-    // n-tiles of a block (same A rows) and consecutive blocks of an expert
-    // (same weights) meet in one L2.
+    // Work queue x = blockIdx.x % 8: with round-robin dispatch of workgroups
+    // over the XCDs all of a queue's workgroups share one L2. Correctness
+    // does not depend on that mapping: every queue has grid / 8 workgroups.
+    const int queue = blockIdx.x % kXcds;
+    int32_t* ctr = args.sched + queue;
     const int n_tiles = args.N / BN;
-    const int live = (args.num_blocks[0] + args.shared_blocks) * n_tiles;
-    const int per_xcd = (live + kXcds - 1) / kXcds;
-    const int slot = blockIdx.x / kXcds;
-    const int tile = (blockIdx.x % kXcds) * per_xcd + slot;
-    if (slot >= per_xcd || tile >= live) return;
-    const int blk = tile / n_tiles;
-    const int n0 = (tile % n_tiles) * BN;
+    const int nb_total = args.shared_blocks + args.num_blocks[0];
+    const int q_items = (nb_total > queue ? (nb_total - queue + kXcds - 1) / kXcds : 0) * n_tiles;
+    const int n_slabs = args.N / kPackRows;
+    const size_t slab_bytes = (size_t)(args.K / 64) * kPackBlock;
 
-    // Which rows, which expert.
-    int r0, r_end;
-    bool shared;
-    int e = 0;
-    if (blk < args.num_blocks[0]) {
-        e = args.block_expert[blk];
-        r0 = args.block_row0[blk];
-        r_end = args.offsets[e + 1];
-        shared = false;
-    } else {
-        r0 = args.P + (blk - args.num_blocks[0]) * BM;
-        r_end = args.P + args.T;
-        shared = true;
-    }
-    const int rows = min(BM, r_end - r0);
-    const int K = args.K;
+    int c = grab(ctr, &s_next);
+    while (c < q_items) {
+        const int vb = queue + kXcds * (c / n_tiles);
+        const int nt = c % n_tiles;
+        // Which rows, which expert.
+        int r0, r_end, e = 0;
+        bool shared;
+        if (vb < args.shared_blocks) {
+            r0 = args.P + vb * BM;
+            r_end = args.P + args.T;
+            shared = true;
+        } else {
+            const int blk = args.block_order[vb - args.shared_blocks];
+            e = args.block_expert[blk];
+            r0 = args.block_row0[blk];
+            r_end = args.offsets[e + 1];
+            shared = false;
+        }
+        const int rows = min(BM, r_end - r0);
+        const int K = args.K;
 
-    LoadPlan<MI> lp;
-    // A loads: load j of wavefront w fills LDS rows 32j + 8w + lane/8,
-    // physical chunk lane%8, which holds logical chunk (lane%8) ^ (row & 7).
-    // Rows past the block read the block's first row: their products land in
-    // output rows that are never stored.
-    lp.a_base = reinterpret_cast<const char*>(args.a);
+        LoadPlan<MI> lp;
+        // A loads: load j of wavefront w fills LDS rows 32j + 8w + lane/8,
+        // physical chunk lane%8, which holds logical chunk swz(row, lane%8).
+        // Rows past the block read the block's first row: their products land
+        // in output rows that are never stored.
+        lp.a_base = reinterpret_cast<const char*>(args.a);
 #pragma unroll
-    for (int j = 0; j < MI; ++j) {
-        const int row = 32 * j + 8 * (int)wave + lane / 8;
-        const int r = r0 + (row < rows ? row : 0);
-        int src_row = r;
-        if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
-        lp.a_off[j] = (uint32_t)src_row * (uint32_t)(K * 2) + (uint32_t)(((lane % 8) ^ (row & 7)) * 16);
-    }
-    // Weight loads. The workgroup's 256 weight rows: gate/up -> rows n0.. of
-    // the gate matrix then the same rows of the up matrix; down -> rows n0..
-    // of W_down. Load j of wavefront w covers 64 consecutive slots
-    // c = 64 (2w + j) + lane: for weights slot (half, row) = (c / 256, c % 256),
-    // for scales c < 256 and biases c >= 256, row c % 256. Each load stays in
-    // one matrix, so its base is uniform.
-    const size_t mat = shared ? 0 : (size_t)e * args.N;
+        for (int j = 0; j < MI; ++j) {
+            const int row = 32 * j + 8 * (int)wave + lane / 8;
+            const int r = r0 + (row < rows ? row : 0);
+            int src_row = r;
+            if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
+            lp.a_off[j] = (uint32_t)src_row * (uint32_t)(K * 2) + (uint32_t)(swz(row, lane % 8) * 16);
+        }
+        // Weight slab wb = wave / 2 of the workgroup: gate/up -> slab nt of
+        // the gate (wb = 0) or up (wb = 1) stack; down -> slab 2 nt + wb.
+        const int wb = (int)(wave >> 1);
+        const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
+        const int slab = GATED ? nt : 2 * nt + wb;
+        lp.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes;
+
+        const int n0 = nt * BN;
+        int brow[2], col0[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int c0 = 64 * (2 * (int)wave + j);        // uniform
-        const int r_loc = (c0 % 256) + lane;
-        const int m = GATED ? (c0 % 256) / 128 : 0;      // uniform
-        const int n_in = GATED ? r_loc % 128 : r_loc;    // row inside the workgroup's span
-        const uint8_t* qm = shared ? args.sq[m] : args.q[m];
-        lp.q_base[j] = reinterpret_cast<const char*>(qm + (mat + n0) * (K / 2)) + (c0 / 256) * 16;
-        lp.q_off[j] = (uint32_t)n_in * (uint32_t)(K / 2);
-        const bool is_bias = c0 >= 256;
-        const uint16_t* sm = is_bias ? (shared ? args.sbi[m] : args.bi[m])
-                                     : (shared ? args.ssc[m] : args.sc[m]);
-        lp.sb_base[j] = reinterpret_cast<const char*>(sm + (mat + n0) * (K / 64));
-        lp.sb_off[j] = (uint32_t)n_in * (uint32_t)(K / 64) * 2u;
-    }
-    int brow[2], col0[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        brow[g] = GATED ? 128 * g + 32 * (int)wave + lane % 32 : 64 * (int)wave + 32 * g + lane % 32;
-        col0[g] = GATED ? n0 + 32 * (int)wave : n0 + 64 * (int)wave + 32 * g;
+        for (int g = 0; g < 2; ++g) {
+            brow[g] = GATED ? 128 * g + 32 * (int)wave + lane % 32 : 64 * (int)wave + 32 * g + lane % 32;
+            col0[g] = GATED ? n0 + 32 * (int)wave : n0 + 64 * (int)wave + 32 * g;
+        }
+
+        // Only the 32-row sub-tiles that hold rows of the block are loaded and
+        // multiplied.
+        const int mia = (rows + 31) / 32;
+        if (mia >= MI) c = gemm_main<BM, GATED, MI>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
+        else if (mia == 1) c = gemm_main<BM, GATED, 1>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
+        else if (mia == 2) c = gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
+        else c = gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
     }
 
-    // Only the 32-row sub-tiles that hold rows of the block are loaded and
-    // multiplied.
-    const int mia = (rows + 31) / 32;
-    if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, lp, wave, r0, rows, brow, col0);
-    else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, lp, wave, r0, rows, brow, col0);
-    else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, lp, wave, r0, rows, brow, col0);
-    else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, lp, wave, r0, rows, brow, col0);
+    // Every queue item has been taken once each workgroup has seen its queue
+    // run out; the last workgroup to get here clears the counters for the
+    // next launch.
+    if (tid == 0 && atomicAdd(args.sched + kXcds, 1) == (int)gridDim.x - 1) {
+        for (int i = 0; i <= kXcds; ++i) atomicExch(args.sched + i, 0);
+    }
+}
+
+// One thread per (expert, row, group): the row's 32 q bytes of the group go
+// to the two halves of its packed block, the scale and bias behind them.
+__global__ void __launch_bounds__(256) pack_w4_kernel(const uint8_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ scale,
+                                                      const uint16_t* __restrict__ bias, int n,
+                                                      int N, int K, char* __restrict__ out) {
+    const int groups = K / 64;
+    const long total = (long)n * N * groups;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const long er = idx / groups;  // e * N + row
+    const int g = (int)(idx - er * groups);
+    const int row = (int)(er % N);
+    const long e = er / N;
+    char* blk = out + ((e * (N / kPackRows) + row / kPackRows) * groups + g) * (long)kPackBlock;
+    const int r = row % kPackRows;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + er * (K / 2) + g * 32);
+    *reinterpret_cast<u32x4*>(blk + r * 16) = src[0];
+    *reinterpret_cast<u32x4*>(blk + (kPackRows + r) * 16) = src[1];
+    *reinterpret_cast<uint16_t*>(blk + kPackQ + r * 2) = scale[idx];
+    *reinterpret_cast<uint16_t*>(blk + kPackQ + 2 * kPackRows + r * 2) = bias[idx];
 }
 
 // out[t] = bf16(y[P + t] + sum_j w[t, j] * y[pair_rows[t * topk + j]]), fp32,
@@ -444,38 +511,55 @@ size_t forward_workspace_bytes(const lily_moe_dims& d) {
     return align_up(rows * d.F * sizeof(uint16_t)) + align_up(rows * d.H * sizeof(float));
 }
 
-static GemmArgs routing_args(const lily_moe_dims& d, const lily_moe_routing& r, int max_blocks) {
+static GemmArgs routing_args(const lily_moe_dims& d, const lily_moe_routing& r) {
     GemmArgs g{};
     g.topk = d.topk;
     g.block_expert = r.block_expert;
     g.block_row0 = r.block_row0;
+    g.block_order = r.block_order;
     g.num_blocks = r.num_blocks;
     g.offsets = r.offsets;
-    g.max_blocks = max_blocks;
     g.P = d.T * d.topk;
     g.T = d.T;
     return g;
 }
 
-// Grid: enough workgroups for the largest possible block map (the live
-// count is only known on the device), a multiple of the XCD count.
+// Persistent grid: the workgroups that fit on the device at once (from the
+// kernel's own occupancy), fewer if the largest possible block map has
+// fewer tiles, a multiple of the queue count.
 template <int BM, bool GATED>
-static dim3 gemm_grid(GemmArgs& g) {
+static int gemm_grid(GemmArgs& g, int max_blocks) {
+    constexpr int kMaxDevices = 64;
+    static int resident[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int slots = dev < kMaxDevices ? resident[dev] : 0;
+    if (slots == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_w4_gemm<BM, GATED>,
+                                                         kGemmThreads, 0) != hipSuccess)
+            per_cu = 0;
+        slots = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+        if (dev < kMaxDevices) resident[dev] = slots;
+    }
     g.shared_blocks = (g.T + BM - 1) / BM;
-    const long tiles = (long)(g.max_blocks + g.shared_blocks) * (g.N / GemmShape<GATED>::BN);
-    return dim3((unsigned)((tiles + kXcds - 1) / kXcds * kXcds));
+    const long tiles = (long)(max_blocks + g.shared_blocks) * (g.N / GemmShape<GATED>::BN);
+    const long grid = tiles < slots ? tiles : slots;
+    return (int)((grid + kXcds - 1) / kXcds * kXcds);
 }
 
 template <int BM>
-static int launch_gate_up_bm(const lily_moe_dims& d, GemmArgs g, hipStream_t stream) {
-    const dim3 grid = gemm_grid<BM, true>(g);
+static int launch_gate_up_bm(GemmArgs g, int max_blocks, hipStream_t stream) {
+    const dim3 grid(gemm_grid<BM, true>(g, max_blocks));
     hipLaunchKernelGGL((moe_w4_gemm<BM, true>), grid, dim3(kGemmThreads), 0, stream, g);
     return check_launch("gate_up_gemm");
 }
 
 template <int BM>
-static int launch_down_bm(const lily_moe_dims& d, GemmArgs g, hipStream_t stream) {
-    const dim3 grid = gemm_grid<BM, false>(g);
+static int launch_down_bm(GemmArgs g, int max_blocks, hipStream_t stream) {
+    const dim3 grid(gemm_grid<BM, false>(g, max_blocks));
     hipLaunchKernelGGL((moe_w4_gemm<BM, false>), grid, dim3(kGemmThreads), 0, stream, g);
     return check_launch("down_gemm");
 }
@@ -483,20 +567,21 @@ static int launch_down_bm(const lily_moe_dims& d, GemmArgs g, hipStream_t stream
 // G1 + G2 (and the shared expert's rows): h = bf16(silu(x Wg^T) * (x Wu^T)).
 int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
                    const lily_moe_routing& r, int max_blocks, uint16_t* h, hipStream_t stream) {
-    GemmArgs g = routing_args(d, r, max_blocks);
+    GemmArgs g = routing_args(d, r);
     g.a = x;
     g.sorted_pairs = r.sorted_pairs;
-    g.q[0] = w.gate.q; g.sc[0] = w.gate.scale; g.bi[0] = w.gate.bias;
-    g.q[1] = w.up.q;   g.sc[1] = w.up.scale;   g.bi[1] = w.up.bias;
-    g.sq[0] = w.sh_gate.q; g.ssc[0] = w.sh_gate.scale; g.sbi[0] = w.sh_gate.bias;
-    g.sq[1] = w.sh_up.q;   g.ssc[1] = w.sh_up.scale;   g.sbi[1] = w.sh_up.bias;
+    g.w[0] = static_cast<const char*>(w.gate);
+    g.w[1] = static_cast<const char*>(w.up);
+    g.sw[0] = static_cast<const char*>(w.sh_gate);
+    g.sw[1] = static_cast<const char*>(w.sh_up);
     g.N = d.F;
     g.K = d.H;
+    g.sched = r.sched;
     g.h_out = h;
     switch (d.tile_m) {
-        case 32: return launch_gate_up_bm<32>(d, g, stream);
-        case 64: return launch_gate_up_bm<64>(d, g, stream);
-        case 128: return launch_gate_up_bm<128>(d, g, stream);
+        case 32: return launch_gate_up_bm<32>(g, max_blocks, stream);
+        case 64: return launch_gate_up_bm<64>(g, max_blocks, stream);
+        case 128: return launch_gate_up_bm<128>(g, max_blocks, stream);
     }
     return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
 }
@@ -504,19 +589,32 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
 // G3 (and the shared expert's rows): y = h Wd^T in fp32.
 int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* h,
                 const lily_moe_routing& r, int max_blocks, float* y, hipStream_t stream) {
-    GemmArgs g = routing_args(d, r, max_blocks);
+    GemmArgs g = routing_args(d, r);
     g.a = h;
-    g.q[0] = w.down.q; g.sc[0] = w.down.scale; g.bi[0] = w.down.bias;
-    g.sq[0] = w.sh_down.q; g.ssc[0] = w.sh_down.scale; g.sbi[0] = w.sh_down.bias;
+    g.w[0] = g.w[1] = static_cast<const char*>(w.down);
+    g.sw[0] = g.sw[1] = static_cast<const char*>(w.sh_down);
     g.N = d.H;
     g.K = d.F;
+    g.sched = r.sched + LILY_SCHED_INTS / 2;
     g.y_out = y;
     switch (d.tile_m) {
-        case 32: return launch_down_bm<32>(d, g, stream);
-        case 64: return launch_down_bm<64>(d, g, stream);
-        case 128: return launch_down_bm<128>(d, g, stream);
+        case 32: return launch_down_bm<32>(g, max_blocks, stream);
+        case 64: return launch_down_bm<64>(g, max_blocks, stream);
+        case 128: return launch_down_bm<128>(g, max_blocks, stream);
     }
     return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
+}
+
+size_t packed_w4_bytes(int n, int N, int K) {
+    return (size_t)n * N * K / 64 * (kPackBlock / kPackRows);
+}
+
+int launch_pack(const lily_w4& w, int n, int N, int K, void* packed, hipStream_t stream) {
+    const long total = (long)n * N * (K / 64);
+    const long grid = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w.q, w.scale,
+                       w.bias, n, N, K, static_cast<char*>(packed));
+    return check_launch("pack_w4");
 }
 
 // G5: weighted gather-combine.

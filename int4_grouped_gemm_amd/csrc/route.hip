@@ -22,7 +22,11 @@
 //                 of e in this span); inside a chunk the earlier pairs come
 //                 from a per-expert token bitmask. This is a stable counting
 //                 sort whose result does not depend on the order of any
-//                 atomic: deterministic and bit-exact.
+//                 atomic: deterministic and bit-exact. It also writes the
+//                 schedule of the grouped GEMMs (block_order: full blocks in
+//                 block order, then each expert's last, partial block by
+//                 descending size class, ties in expert order) and clears
+//                 their work-queue counters.
 // For small T the top-k runs inside route_finish and the route is one launch.
 #include "common.hpp"
 
@@ -134,17 +138,44 @@ __global__ void __launch_bounds__(kTopkThreads) route_topk_kernel(
     }
 }
 
+// Exclusive prefix sum of one value per thread over the 1024-thread
+// workgroup, in thread order; *total receives the sum of all values. Every
+// thread of the workgroup must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int32_t* s_wsum, int* total) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int r = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += r;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < kFinishWaves; ++w) {
+        const int sw = s_wsum[w];
+        if (w < wave) base += sw;
+        tot += sw;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + inc - v;
+}
+
 __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     const float* __restrict__ logits, int T, int E, int k, int M, int fused_topk,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_rows, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ block_row0, int32_t* __restrict__ num_blocks) {
+    int32_t* __restrict__ block_row0, int32_t* __restrict__ num_blocks,
+    int32_t* __restrict__ block_order, int32_t* __restrict__ sched) {
     __shared__ int32_t hist[kFinishWaves][kMaxExperts];    // rows per span, then cursors
     __shared__ uint32_t cmask[kFinishWaves][kMaxExperts];  // tokens of a chunk, per expert
     __shared__ int32_t s_off[kMaxExperts + 1];             // row offsets
     __shared__ int32_t s_bst[kMaxExperts + 1];             // block starts
-    __shared__ int32_t s_wsum[2][kFinishWaves];
+    __shared__ int32_t s_fst[kMaxExperts];                 // full blocks of earlier experts
+    __shared__ int32_t s_wsum[kFinishWaves];
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -201,42 +232,39 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     }
     __syncthreads();
 
-    // Exclusive scans of rows (s_off) and blocks (s_bst) over the experts:
-    // each thread owns one expert (E <= 512 < 1024 threads).
+    // Exclusive scans over the experts, one expert per thread (E <= 512 <
+    // 1024 threads): rows (s_off), blocks (s_bst), full blocks (s_fst), and
+    // for the schedule the experts whose partial block falls in each size
+    // class.
     {
         const int e = tid;
-        const int v_rows = e < E ? s_off[e] : 0;
-        const int v_blks = e < E ? s_bst[e] : 0;
-        int inc_r = v_rows, inc_b = v_blks;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int r = __shfl_up(inc_r, off, kWave);
-            const int b = __shfl_up(inc_b, off, kWave);
-            if (lane >= off) {
-                inc_r += r;
-                inc_b += b;
-            }
+        const int rows_e = e < E ? s_off[e] : 0;
+        const int full_e = rows_e / M;
+        const int rem_e = rows_e - full_e * M;
+        const int cls_e = rem_e > 0 ? (4 * rem_e + M - 1) / M : 0;  // 1..4: quarter of a block
+        int tot_rows, tot_blks, tot_full;
+        const int ex_rows = block_exclusive_scan(rows_e, s_wsum, &tot_rows);
+        const int ex_blks = block_exclusive_scan(e < E ? s_bst[e] : 0, s_wsum, &tot_blks);
+        const int ex_full = block_exclusive_scan(full_e, s_wsum, &tot_full);
+        int cls_rank = 0, cls_base = tot_full;
+        for (int c = 4; c >= 1; --c) {
+            int tot_c;
+            const int ex_c = block_exclusive_scan(cls_e == c ? 1 : 0, s_wsum, &tot_c);
+            if (cls_e == c) cls_rank = cls_base + ex_c;
+            if (cls_e < c) cls_base += tot_c;
         }
-        if (lane == kWave - 1) {
-            s_wsum[0][wave] = inc_r;
-            s_wsum[1][wave] = inc_b;
-        }
-        __syncthreads();
-        int base_r = 0, base_b = 0;
-        for (int w = 0; w < wave; ++w) {
-            base_r += s_wsum[0][w];
-            base_b += s_wsum[1][w];
-        }
-        __syncthreads();
         if (e < E) {
-            s_off[e] = base_r + inc_r - v_rows;
-            s_bst[e] = base_b + inc_b - v_blks;
+            s_off[e] = ex_rows;
+            s_bst[e] = ex_blks;
+            s_fst[e] = ex_full;
+            if (rem_e > 0) block_order[cls_rank] = ex_blks + full_e;
         }
-        if (e == E - 1) {
-            s_off[E] = base_r + inc_r;
-            s_bst[E] = base_b + inc_b;
+        if (e == 0) {
+            s_off[E] = tot_rows;
+            s_bst[E] = tot_blks;
         }
     }
+    if (tid < kSchedInts) sched[tid] = 0;
     __syncthreads();
 
     for (int e = tid; e <= E; e += kFinishThreads) offsets[e] = s_off[e];
@@ -252,6 +280,8 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
         }
         block_expert[b] = lo;
         block_row0[b] = s_off[lo] + (b - s_bst[lo]) * M;
+        const int j = b - s_bst[lo];
+        if (j < (s_off[lo + 1] - s_off[lo]) / M) block_order[s_fst[lo] + j] = b;
     }
 
     // Pass 2: stable positions. The k experts of a token are distinct, so
@@ -301,7 +331,8 @@ int launch_route(const lily_moe_dims& d, const float* logits, const lily_moe_rou
     }
     hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(kFinishThreads), 0, stream, logits, d.T,
                        d.E, d.topk, d.tile_m, fused, r.topk_ids, r.topk_w, r.counts, r.offsets,
-                       r.sorted_pairs, r.pair_rows, r.block_expert, r.block_row0, r.num_blocks);
+                       r.sorted_pairs, r.pair_rows, r.block_expert, r.block_row0, r.num_blocks,
+                       r.block_order, r.sched);
     return check_launch("route_finish");
 }
 

@@ -30,12 +30,25 @@ def route_gpu(d: L.LilyMoeDims, logits: np.ndarray, device="cuda"):
 def routing_to_host(r: L.Routing) -> dict:
     out = {n: getattr(r, n).cpu().numpy() for n in L.ROUTING_FIELDS}
     nb = int(out["num_blocks"][0])
-    out["block_expert"] = out["block_expert"][:nb]
-    out["block_row0"] = out["block_row0"][:nb]
+    for key in ("block_expert", "block_row0", "block_order"):
+        out[key] = out[key][:nb]
     return out
 
 
-def compare_routing(gpu: dict, ref: dict) -> None:
+def expected_block_order(ref: dict, tile_m: int) -> np.ndarray:
+    """The GEMM schedule the header documents, from a block map: the full
+    blocks in block order, then the partial blocks (each expert's last) by
+    descending class ceil(4 rows / tile_m), ties in expert order."""
+    nb = int(ref["num_blocks"][0])
+    be = np.asarray(ref["block_expert"][:nb])
+    rows = np.minimum(tile_m, np.asarray(ref["offsets"])[be + 1] - np.asarray(ref["block_row0"][:nb]))
+    full = [b for b in range(nb) if rows[b] == tile_m]
+    part = sorted((b for b in range(nb) if rows[b] < tile_m),
+                  key=lambda b: (-((4 * int(rows[b]) + tile_m - 1) // tile_m), int(be[b])))
+    return np.array(full + part, np.int32)
+
+
+def compare_routing(gpu: dict, ref: dict, tile_m: int = None) -> None:
     for k in ROUTE_KEYS:
         assert np.array_equal(gpu[k], ref[k]), f"routing {k} differs at " \
             f"{np.argwhere(np.asarray(gpu[k]) != np.asarray(ref[k]))[:5].tolist()}"
@@ -43,6 +56,10 @@ def compare_routing(gpu: dict, ref: dict) -> None:
     assert np.array_equal(gpu["block_expert"], ref["block_expert"]), "block_expert"
     assert np.array_equal(gpu["block_row0"], ref["block_row0"]), "block_row0"
     assert np.max(np.abs(gpu["topk_w"] - ref["topk_w"])) <= 2e-6, "topk_w"
+    if tile_m is not None:
+        want = expected_block_order(ref, tile_m)
+        assert np.array_equal(gpu["block_order"], want), "block_order"
+        assert not np.any(gpu["sched"]), "route must leave the GEMM queue counters zero"
 
 
 def forward_gpu(d: L.LilyMoeDims, w: L.Weights, x: torch.Tensor, r: L.Routing,

@@ -50,8 +50,7 @@ def routing(fake=FAKE, **over):
 
 
 def weights(**over):
-    w = {n: L.LilyW4(FAKE, FAKE + 256, FAKE + 512) for n in
-         ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")}
+    w = {n: FAKE + 4096 * i for i, n in enumerate(L.WEIGHT_FIELDS)}
     w.update(over)
     return L.LilyMoeWeights(**w)
 
@@ -117,10 +116,13 @@ def test_forward_rejects(lib):
     assert call_forward(lib, good_dims(), x=None) == L.LILY_ERR_INVALID_ARG
     assert call_forward(lib, good_dims(), out=FAKE + 2) == L.LILY_ERR_INVALID_ARG
     assert call_forward(lib, good_dims(), ws=None) == L.LILY_ERR_INVALID_ARG
-    for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
-        w = weights(**{n: L.LilyW4(FAKE, None, FAKE)})
+    for n in L.WEIGHT_FIELDS:
+        w = weights(**{n: None})
         assert call_forward(lib, good_dims(), w=w) == L.LILY_ERR_INVALID_ARG
         assert n in lib.lily_last_error().decode()
+        w = weights(**{n: FAKE + 8})
+        assert call_forward(lib, good_dims(), w=w) == L.LILY_ERR_INVALID_ARG
+        assert "aligned" in lib.lily_last_error().decode()
     d = good_dims()
     need = lib.lily_moe_workspace_bytes(ctypes.byref(d))
     assert call_forward(lib, d, nbytes=need - 1) == L.LILY_ERR_WORKSPACE
@@ -140,3 +142,24 @@ def test_binding_raises(lib):
     with pytest.raises(L.LilyError) as ei:
         L.lily_moe_max_blocks(good_dims(topk=99))
     assert ei.value.code == L.LILY_ERR_INVALID_ARG
+
+
+def test_packed_bytes(lib):
+    assert lib.lily_w4_packed_bytes(256, 512, 2048, 64) == 256 * 512 * 2048 * 9 // 16
+    assert lib.lily_w4_packed_bytes(1, 128, 64, 64) == 4608
+    for bad in [(0, 128, 64, 64), (1, 100, 64, 64), (1, 128, 96, 64), (1, 128, 64, 32),
+                (1, -128, 64, 64)]:
+        assert lib.lily_w4_packed_bytes(*bad) == 0, bad
+
+
+def test_pack_rejects(lib):
+    w = L.LilyW4(FAKE, FAKE + 256, FAKE + 512)
+    pack = lib.lily_w4_pack
+    assert pack(ctypes.byref(w), 1, 100, 64, 64, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert "multiple of 128" in lib.lily_last_error().decode()
+    assert pack(None, 1, 128, 64, 64, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert pack(ctypes.byref(w), 1, 128, 64, 64, None, None) == L.LILY_ERR_INVALID_ARG
+    assert "packed" in lib.lily_last_error().decode()
+    bad = L.LilyW4(FAKE, FAKE + 2, FAKE)
+    assert pack(ctypes.byref(bad), 1, 128, 64, 64, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert "scale" in lib.lily_last_error().decode()

@@ -73,7 +73,7 @@ def run_chain(cfg, chunks, sample, tile_m=128, n_layers=None):
             L.lily_moe_forward(d, w, gpu_x[ci], rt, out, ws)
             L.lily_residual_norm(T, cfg.H, gpu_r[ci], out, gpu_x[ci], EPS)
             torch.cuda.synchronize()
-            G.compare_routing(G.routing_to_host(rt), ref_r)
+            G.compare_routing(G.routing_to_host(rt), ref_r, tile_m)
             ids_s.append(ref_r["topk_ids"][sample])
             wts_s.append(ref_r["topk_w"][sample])
             got.append(G.from_dev_bits(out)[sample])
