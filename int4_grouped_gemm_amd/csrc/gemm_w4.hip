@@ -110,6 +110,11 @@ __device__ __forceinline__ void dequant8(uint32_t v, float s512, float b, uint32
 // is the 16-byte chunk 4h + s of its row.
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
+// Workgroups whose own queue is empty take items from the other queues.
+// Off: at the end of a launch the idle workgroups of drained queues would
+// all contend for the few remaining counters, which costs more than the
+// imbalance between queues.
+constexpr bool kSteal = false;
 
 template <bool GATED>
 struct GemmShape {
@@ -162,44 +167,87 @@ __device__ __forceinline__ void barrier_only() {
     asm volatile("" ::: "memory");
 }
 
+// A wave-uniform pointer, made explicit so that it lives in SGPRs.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Global -> LDS load (gfx950 LDS DMA) with a wave-uniform 64-bit base in
 // SGPRs and a 32-bit per-lane byte offset; lane l lands at LDS address
 // m0 + l * size. The kernel's own code uses M0 for nothing else.
 __device__ __forceinline__ void dma16(const void* base, uint32_t lane_off, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds_addr), "v"(lane_off), "s"(base) : "memory");
+                 :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
+                    "s"(uniform_ptr(base)) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t lane_off, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-                 :: "s"(lds_addr), "v"(lane_off), "s"(base) : "memory");
+                 :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
+                    "s"(uniform_ptr(base)) : "memory");
 }
 
 // Next item of a work queue, the same value in every thread of the
-// workgroup. The first barrier keeps the slot from being overwritten while
-// a wavefront still reads the previous value.
-__device__ __forceinline__ int grab(int32_t* ctr, int* s_next) {
-    __syncthreads();
-    if (threadIdx.x == 0) *s_next = atomicAdd(ctr, 1);
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(*s_next);
+// workgroup. Consecutive calls alternate between two LDS slots, so a slot is
+// rewritten only after the barrier of the following call, which every
+// wavefront reaches after reading it. Only LDS is waited for: DMA loads in
+// flight stay in flight.
+__device__ __forceinline__ int grab(int32_t* ctr, int* s_slot, int& toggle) {
+    int* slot = s_slot + toggle;
+    toggle ^= 1;
+    if (threadIdx.x == 0) *slot = atomicAdd(ctr, 1);
+    wait_lgkmcnt0();
+    barrier_only();
+    return __builtin_amdgcn_readfirstlane(*slot);
 }
 
-// Per-tile load plan of one wavefront: the A row offsets of its DMA loads
-// and the packed block of its weight slab at k-step 0 (+ kt * kPackBlock).
+// One work item (a (block, n-tile) tile) and the load plan of one
+// wavefront for it: the A row offsets of its DMA loads and the packed block
+// of its weight slab at k-step 0 (+ kt * kPackBlock).
 template <int MI>
-struct LoadPlan {
+struct Item {
+    bool valid;
+    bool prefetched;         // its first NS - 1 stages are already in flight
+    int r0, rows, n0;
+    int mia;                 // 32-row sub-tiles that hold rows: min(MI, ceil(rows / 32))
     const char* a_base;      // A rows: + kt * 128
     uint32_t a_off[MI];      // row byte offset + swizzled chunk
     const char* w_base;
 };
 
-// Loads, multiplies and stores one tile; returns the workgroup's next queue
-// item, taken after the k-loop so that its latency overlaps the stores.
-template <int BM, bool GATED, int MIA>
-__device__ __forceinline__ int gemm_main(const GemmArgs& args, char* smem_p,
-                                         const LoadPlan<BM / 32>& lp, uint32_t wave, int r0,
-                                         int rows, const int* brow, const int* col0,
-                                         int32_t* ctr, int* s_next) {
+// DMA of one k-step stage of an item by one wavefront: its n_a A loads
+// (8 rows each, n_a <= MI), then half wh of weight slab wb (rows 0-63 and
+// 64-127, 1 KB each) and the slab's 128 scales (wh = 0) or biases (wh = 1).
+// N_DMA = n_a + 3 loads in all.
+template <int BM>
+__device__ __forceinline__ void issue_stage(const Item<BM / 32>& it, int n_a, int kt, int buf,
+                                            uint32_t smem, uint32_t wave, int lane) {
+    using Ld = Lds<BM>;
+#pragma unroll
+    for (int j = 0; j < BM / 32; ++j)
+        if (j < n_a)
+            dma16(it.a_base + kt * 128, it.a_off[j],
+                  smem + Ld::A_OFF + buf * Ld::A + (32 * j + 8 * wave) * 128);
+    const uint32_t wh = wave & 1u, wb = wave >> 1;
+    const uint32_t q_off = (wh * 128u + (uint32_t)lane) * 16u;
+    const uint32_t sb_off = (uint32_t)kPackQ + wh * 256u + (uint32_t)lane * 4u;
+    const uint32_t q_lds = smem + Ld::Q_OFF + buf * Ld::Q + (wh * 256u + wb * 128u) * 16u;
+    const uint32_t sb_lds = smem + Ld::SB_OFF + buf * Ld::SB + wh * 512u + wb * 256u;
+    const char* blk = it.w_base + (size_t)kt * kPackBlock;
+    dma16(blk, q_off, q_lds);
+    dma16(blk, q_off + 64 * 16, q_lds + 64 * 16);
+    dma4(blk, sb_off, sb_lds);
+}
+
+// Loads, multiplies and stores one tile. `prep_next` runs between the
+// k-loop and the stores: it takes and resolves the workgroup's next item, so
+// that the latency of its metadata loads overlaps the stores.
+template <int BM, bool GATED, int MIA, typename PrepNext>
+__device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
+                                          const Item<BM / 32>& lp, uint32_t wave,
+                                          PrepNext&& prep_next) {
     using Ld = Lds<BM>;
     constexpr int NS = Ld::NS;
     constexpr int NI = 2;
@@ -210,25 +258,15 @@ __device__ __forceinline__ int gemm_main(const GemmArgs& args, char* smem_p,
     const int lane = threadIdx.x % kWave;
     const int h = lane / 32;
     const int nk = args.K / 64;
-
-    // Weight DMA of this wavefront: half wh of slab wb, rows 0-63 and 64-127
-    // (1 KB each), and the 128 scales (wh = 0) or biases (wh = 1).
-    const uint32_t wh = wave & 1u, wb = wave >> 1;
-    const uint32_t q_off = (wh * 128u + (uint32_t)lane) * 16u;
-    const uint32_t sb_off = (uint32_t)kPackQ + wh * 256u + (uint32_t)lane * 4u;
-    const uint32_t q_lds = smem + Ld::Q_OFF + (wh * 256u + wb * 128u) * 16u;
-    const uint32_t sb_lds = smem + Ld::SB_OFF + wh * 512u + wb * 256u;
-
-    auto issue = [&](int kt, int buf) {
+    const int r0 = lp.r0, rows = lp.rows;
+    int brow[2], col0[2];
 #pragma unroll
-        for (int j = 0; j < N_A; ++j)
-            dma16(lp.a_base + kt * 128, lp.a_off[j],
-                  smem + Ld::A_OFF + buf * Ld::A + (32 * j + 8 * wave) * 128);
-        const char* blk = lp.w_base + (size_t)kt * kPackBlock;
-        dma16(blk, q_off, q_lds + buf * Ld::Q);
-        dma16(blk, q_off + 64 * 16, q_lds + buf * Ld::Q + 64 * 16);
-        dma4(blk, sb_off, sb_lds + buf * Ld::SB);
-    };
+    for (int g = 0; g < 2; ++g) {
+        brow[g] = GATED ? 128 * g + 32 * (int)wave + lane % 32 : 64 * (int)wave + 32 * g + lane % 32;
+        col0[g] = GATED ? lp.n0 + 32 * (int)wave : lp.n0 + 64 * (int)wave + 32 * g;
+    }
+
+    auto issue = [&](int kt, int buf) { issue_stage<BM>(lp, MIA, kt, buf, smem, wave, lane); };
 
     f32x16 acc[MIA][NI];
 #pragma unroll
@@ -329,15 +367,23 @@ __device__ __forceinline__ int gemm_main(const GemmArgs& args, char* smem_p,
         wait_lgkmcnt0();  // this wavefront's LDS reads of the stage are done
     };
 
-    issue(0, 0);
-    if (NS == 3 && nk > 1) issue(1, 1);
-    for (int kt = 0; kt < nk; kt += NS) {
-#pragma unroll
-        for (int u = 0; u < NS; ++u)
-            if (kt + u < nk) step(kt + u, u);
+    if (!lp.prefetched) {
+        issue(0, 0);
+        if (NS == 3 && nk > 1) issue(1, 1);
     }
+    // Whole rounds of NS steps, then the remaining steps (buffers 0, 1, ..):
+    // no step of the main loop is conditional, so the accumulators keep
+    // their registers across the back edge.
+    int kt = 0;
+    for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) step(kt + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+        if (kt + u < nk) step(kt + u, u);
 
-    const int next = grab(ctr, s_next);
+    prep_next();
 
     // Epilogue. C layout of a 32x32 tile: lane l, register r holds row
     // 8*(r/4) + 4*(l/32) + r%4 and column l%32.
@@ -359,7 +405,6 @@ __device__ __forceinline__ int gemm_main(const GemmArgs& args, char* smem_p,
             }
         }
     }
-    return next;
 }
 
 template <int BM, bool GATED>
@@ -367,84 +412,124 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
     constexpr int BN = GemmShape<GATED>::BN;
     constexpr int MI = BM / 32;
     __shared__ __attribute__((aligned(16))) char smem[Lds<BM>::TOTAL];
-    __shared__ int s_next;
+    __shared__ int s_slot[2];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
     // Work queue x = blockIdx.x % 8: with round-robin dispatch of workgroups
-    // over the XCDs all of a queue's workgroups share one L2. Correctness
-    // does not depend on that mapping: every queue has grid / 8 workgroups.
-    const int queue = blockIdx.x % kXcds;
-    int32_t* ctr = args.sched + queue;
+    // over the XCDs all of a queue's workgroups share one L2. A workgroup
+    // drains its own queue, then takes what is left in the others (in
+    // order x + 1, x + 2, ...); each item is taken exactly once through its
+    // queue's counter. Correctness does not depend on the XCD mapping.
     const int n_tiles = args.N / BN;
     const int nb_total = args.shared_blocks + args.num_blocks[0];
-    const int q_items = (nb_total > queue ? (nb_total - queue + kXcds - 1) / kXcds : 0) * n_tiles;
     const int n_slabs = args.N / kPackRows;
     const size_t slab_bytes = (size_t)(args.K / 64) * kPackBlock;
+    int cq = blockIdx.x % kXcds;
+    int tried = 0, toggle = 0;
 
-    int c = grab(ctr, &s_next);
-    while (c < q_items) {
-        const int vb = queue + kXcds * (c / n_tiles);
-        const int nt = c % n_tiles;
-        // Which rows, which expert.
-        int r0, r_end, e = 0;
-        bool shared;
-        if (vb < args.shared_blocks) {
-            r0 = args.P + vb * BM;
-            r_end = args.P + args.T;
-            shared = true;
-        } else {
-            const int blk = args.block_order[vb - args.shared_blocks];
-            e = args.block_expert[blk];
-            r0 = args.block_row0[blk];
-            r_end = args.offsets[e + 1];
-            shared = false;
-        }
-        const int rows = min(BM, r_end - r0);
-        const int K = args.K;
-
-        LoadPlan<MI> lp;
-        // A loads: load j of wavefront w fills LDS rows 32j + 8w + lane/8,
-        // physical chunk lane%8, which holds logical chunk swz(row, lane%8).
-        // Rows past the block read the block's first row: their products land
-        // in output rows that are never stored.
-        lp.a_base = reinterpret_cast<const char*>(args.a);
+    // Items of queue q: its blocks q, q + 8, ... times the n-tiles.
+    auto items_of = [&](int q) {
+        return (nb_total > q ? (nb_total - q + kXcds - 1) / kXcds : 0) * n_tiles;
+    };
+    // Takes the next item of queue cq (one atomic) and resolves its rows,
+    // expert and load plan; it.valid = false if the queue is empty.
+    auto take = [&](Item<MI>& it) {
+        it.valid = false;
+        if (tried >= kXcds) return;
+        const int c = grab(args.sched + cq, s_slot, toggle);
+        if (c >= items_of(cq)) return;
+        {
+            const int vb = cq + kXcds * (c / n_tiles);
+            const int nt = c % n_tiles;
+            int r_end, e = 0;
+            bool shared;
+            if (vb < args.shared_blocks) {
+                it.r0 = args.P + vb * BM;
+                r_end = args.P + args.T;
+                shared = true;
+            } else {
+                const int blk = args.block_order[vb - args.shared_blocks];
+                e = args.block_expert[blk];
+                it.r0 = args.block_row0[blk];
+                r_end = args.offsets[e + 1];
+                shared = false;
+            }
+            it.rows = min(BM, r_end - it.r0);
+            it.mia = min(MI, (it.rows + 31) / 32);
+            it.prefetched = false;
+            it.n0 = nt * BN;
+            // A loads: load j of wavefront w fills LDS rows 32j + 8w +
+            // lane/8, physical chunk lane%8, which holds logical chunk
+            // swz(row, lane%8). Rows past the block read the block's first
+            // row: their products land in output rows that are never
+            // stored.
+            it.a_base = reinterpret_cast<const char*>(args.a);
 #pragma unroll
-        for (int j = 0; j < MI; ++j) {
-            const int row = 32 * j + 8 * (int)wave + lane / 8;
-            const int r = r0 + (row < rows ? row : 0);
-            int src_row = r;
-            if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
-            lp.a_off[j] = (uint32_t)src_row * (uint32_t)(K * 2) + (uint32_t)(swz(row, lane % 8) * 16);
+            for (int j = 0; j < MI; ++j) {
+                const int row = 32 * j + 8 * (int)wave + lane / 8;
+                const int r = it.r0 + (row < it.rows ? row : 0);
+                int src_row = r;
+                if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
+                it.a_off[j] = (uint32_t)src_row * (uint32_t)(args.K * 2) +
+                              (uint32_t)(swz(row, lane % 8) * 16);
+            }
+            // Weight slab wb = wave / 2 of the workgroup: gate/up -> slab
+            // nt of the gate (wb = 0) or up (wb = 1) stack; down -> slab
+            // 2 nt + wb.
+            const int wb = (int)(wave >> 1);
+            const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
+            const int slab = GATED ? nt : 2 * nt + wb;
+            it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes;
+            it.valid = true;
+            return;
         }
-        // Weight slab wb = wave / 2 of the workgroup: gate/up -> slab nt of
-        // the gate (wb = 0) or up (wb = 1) stack; down -> slab 2 nt + wb.
-        const int wb = (int)(wave >> 1);
-        const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
-        const int slab = GATED ? nt : 2 * nt + wb;
-        lp.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes;
+    };
+    // Once the own queue is empty: try the next queues in turn (when
+    // kSteal). Every decision here follows a value that grab() broadcast
+    // through LDS, so all wavefronts take the same path and meet at the
+    // same barriers.
+    auto steal = [&](Item<MI>& it) {
+        while (kSteal && !it.valid) {
+            cq = (cq + 1) % kXcds;
+            if (++tried >= kXcds) return;
+            take(it);
+        }
+    };
 
-        const int n0 = nt * BN;
-        int brow[2], col0[2];
+    const uint32_t smem_addr = (uint32_t)(size_t)smem;
+    Item<MI> cur;
+    take(cur);
+    steal(cur);
+    while (cur.valid) {
+        Item<MI> nxt;
+        // After the k-loop (every wavefront is done with the LDS stages):
+        // take the next item and start its first stages, so that their
+        // latency overlaps this tile's stores.
+        auto prep = [&]() {
+            take(nxt);
+            if (nxt.valid) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            brow[g] = GATED ? 128 * g + 32 * (int)wave + lane % 32 : 64 * (int)wave + 32 * g + lane % 32;
-            col0[g] = GATED ? n0 + 32 * (int)wave : n0 + 64 * (int)wave + 32 * g;
-        }
-
-        // Only the 32-row sub-tiles that hold rows of the block are loaded and
-        // multiplied.
-        const int mia = (rows + 31) / 32;
-        if (mia >= MI) c = gemm_main<BM, GATED, MI>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
-        else if (mia == 1) c = gemm_main<BM, GATED, 1>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
-        else if (mia == 2) c = gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
-        else c = gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, lp, wave, r0, rows, brow, col0, ctr, &s_next);
+                for (int u = 0; u < Lds<BM>::NS - 1; ++u)
+                    if (u < args.K / 64) issue_stage<BM>(nxt, nxt.mia, u, u, smem_addr, wave, lane);
+                nxt.prefetched = true;
+            }
+        };
+        // Only the 32-row sub-tiles that hold rows of the block are loaded
+        // and multiplied.
+        const int mia = cur.mia;
+        if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, cur, wave, prep);
+        else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, cur, wave, prep);
+        else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, cur, wave, prep);
+        else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, cur, wave, prep);
+        steal(nxt);  // after the stores: only the last items of a workgroup get here with nothing
+        cur = nxt;
     }
 
-    // Every queue item has been taken once each workgroup has seen its queue
-    // run out; the last workgroup to get here clears the counters for the
+    // A workgroup gets here once every queue has run out, so when the last
+    // one arrives every item has been taken; it clears the counters for the
     // next launch.
     if (tid == 0 && atomicAdd(args.sched + kXcds, 1) == (int)gridDim.x - 1) {
         for (int i = 0; i <= kXcds; ++i) atomicExch(args.sched + i, 0);

@@ -138,29 +138,48 @@ __global__ void __launch_bounds__(kTopkThreads) route_topk_kernel(
     }
 }
 
-// Exclusive prefix sum of one value per thread over the 1024-thread
-// workgroup, in thread order; *total receives the sum of all values. Every
-// thread of the workgroup must call it.
-__device__ __forceinline__ int block_exclusive_scan(int v, int32_t* s_wsum, int* total) {
+// Inclusive prefix sum over the 64 lanes of a wavefront: DPP shifts inside
+// each row of 16 lanes (out-of-row sources read 0), then the row totals
+// from lanes 15, 31, 47 added to the later rows. No LDS traffic.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr 1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr 2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr 4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr 8
+    const int row = (threadIdx.x % kWave) / 16;
+    const int t0 = __builtin_amdgcn_readlane(x, 15);
+    const int t1 = __builtin_amdgcn_readlane(x, 31);
+    const int t2 = __builtin_amdgcn_readlane(x, 47);
+    return x + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
+// Exclusive prefix sums of NV values per thread over the 1024-thread
+// workgroup, in thread order; tot[i] receives the sum of value i over all
+// threads. The 16 wavefront totals of each value are scanned by the lanes
+// of every wavefront (one LDS read per value). Every thread of the
+// workgroup must call it.
+template <int NV>
+__device__ __forceinline__ void block_exclusive_scan(const int (&v)[NV], int (&ex)[NV],
+                                                     int (&tot)[NV], int32_t* s_wsum) {
+    static_assert(kFinishWaves == 16, "one 16-lane row scans the wavefront totals");
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
-    int inc = v;
+    int inc[NV];
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int r = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += r;
-    }
-    if (lane == kWave - 1) s_wsum[wave] = inc;
-    __syncthreads();
-    int base = 0, tot = 0;
-    for (int w = 0; w < kFinishWaves; ++w) {
-        const int sw = s_wsum[w];
-        if (w < wave) base += sw;
-        tot += sw;
+    for (int i = 0; i < NV; ++i) inc[i] = wave_inclusive_scan(v[i]);
+    if (lane == kWave - 1) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) s_wsum[i * kFinishWaves + wave] = inc[i];
     }
     __syncthreads();
-    *total = tot;
-    return base + inc - v;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int ws = wave_inclusive_scan(lane < kFinishWaves ? s_wsum[i * kFinishWaves + lane] : 0);
+        const int base = wave > 0 ? __builtin_amdgcn_readlane(ws, wave - 1) : 0;
+        tot[i] = __builtin_amdgcn_readlane(ws, kFinishWaves - 1);
+        ex[i] = base + inc[i] - v[i];
+    }
+    __syncthreads();
 }
 
 __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
@@ -175,7 +194,7 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     __shared__ int32_t s_off[kMaxExperts + 1];             // row offsets
     __shared__ int32_t s_bst[kMaxExperts + 1];             // block starts
     __shared__ int32_t s_fst[kMaxExperts];                 // full blocks of earlier experts
-    __shared__ int32_t s_wsum[kFinishWaves];
+    __shared__ int32_t s_wsum[7 * kFinishWaves];
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -242,16 +261,18 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
         const int full_e = rows_e / M;
         const int rem_e = rows_e - full_e * M;
         const int cls_e = rem_e > 0 ? (4 * rem_e + M - 1) / M : 0;  // 1..4: quarter of a block
-        int tot_rows, tot_blks, tot_full;
-        const int ex_rows = block_exclusive_scan(rows_e, s_wsum, &tot_rows);
-        const int ex_blks = block_exclusive_scan(e < E ? s_bst[e] : 0, s_wsum, &tot_blks);
-        const int ex_full = block_exclusive_scan(full_e, s_wsum, &tot_full);
-        int cls_rank = 0, cls_base = tot_full;
+        // values: rows, blocks, full blocks, then one flag per size class 4..1
+        int v[7] = {rows_e, e < E ? s_bst[e] : 0, full_e, cls_e == 4, cls_e == 3, cls_e == 2,
+                    cls_e == 1};
+        int ex[7], tot[7];
+        block_exclusive_scan<7>(v, ex, tot, s_wsum);
+        const int ex_rows = ex[0], ex_blks = ex[1], ex_full = ex[2];
+        const int tot_rows = tot[0], tot_blks = tot[1];
+        int cls_rank = 0, cls_base = tot[2];
+#pragma unroll
         for (int c = 4; c >= 1; --c) {
-            int tot_c;
-            const int ex_c = block_exclusive_scan(cls_e == c ? 1 : 0, s_wsum, &tot_c);
-            if (cls_e == c) cls_rank = cls_base + ex_c;
-            if (cls_e < c) cls_base += tot_c;
+            if (cls_e == c) cls_rank = cls_base + ex[3 + 4 - c];
+            cls_base += tot[3 + 4 - c];
         }
         if (e < E) {
             s_off[e] = ex_rows;
