@@ -100,7 +100,6 @@ def main():
     x = torch.from_numpy(S.activations(cfg).view(np.int16)).to(dev)
     routing = L.alloc_routing(d, dev)
     ws = L.alloc_workspace(d, dev)
-    h, y = L.workspace_views(d, ws)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
@@ -116,13 +115,13 @@ def main():
         L.lily_moe_route(d, logits[layer], routing, stream)
         if ev is not None:
             ev[1].record(stream)
-        L.lily_moe_gate_up(d, w, x, routing, h, stream)
+        L.lily_moe_gate_up(d, w, x, routing, ws, stream)
         if ev is not None:
             ev[2].record(stream)
-        L.lily_moe_down(d, w, h, routing, y, stream)
+        L.lily_moe_down(d, w, routing, ws, stream)
         if ev is not None:
             ev[3].record(stream)
-        L.lily_moe_combine(d, y, routing, out, stream)
+        L.lily_moe_combine(d, routing, ws, out, stream)
         if ev is not None:
             ev[4].record(stream)
 

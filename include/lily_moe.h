@@ -122,12 +122,13 @@ typedef struct {
                               partial block by descending size class
                               ceil(4 rows / tile_m), ties in expert order;
    sched int32 [LILY_SCHED_INTS]
-                              work-queue counters of the grouped GEMMs. Zero
-                              them once after allocating; lily_moe_route
-                              clears them and every GEMM launch leaves them
-                              zero when it completes. Launches that share a
-                              routing buffer must be ordered on one stream. */
-#define LILY_SCHED_INTS 32
+                              work-queue and split-K tile counters of the
+                              grouped GEMMs. Zero them once after
+                              allocating; lily_moe_route clears them and
+                              every GEMM launch leaves them zero when it
+                              completes. Launches that share a routing
+                              buffer must be ordered on one stream. */
+#define LILY_SCHED_INTS 1056
 typedef struct {
     int32_t* topk_ids;
     float* topk_w;
@@ -147,9 +148,13 @@ typedef struct {
 int32_t lily_moe_max_blocks(const lily_moe_dims* dims);
 
 /* Host, pure. Bytes of device workspace lily_moe_forward needs for dims
-   (0 for invalid dims). The workspace holds the SwiGLU intermediate h (bf16)
-   and the per-row expert outputs y (fp32) for the P routed rows and the T
-   shared rows. */
+   (0 for invalid dims). Layout, each part starting on a 256-byte boundary:
+     h     bf16 [P + T, F]: the SwiGLU intermediate (routed rows in expert
+           order, then the shared expert's rows by token);
+     y     fp32 [P + T, H]: the per-row expert outputs, same row order;
+     part  fp32 partial sums of the GEMMs that split K, present only for
+           small block maps (few tokens), where a tile's K is spread over
+           several workgroups. */
 size_t lily_moe_workspace_bytes(const lily_moe_dims* dims);
 
 /* Host, pure. Bytes of the packed layout of an n-expert stack of [N, K]
@@ -192,22 +197,24 @@ int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
 
 /* The three stages of lily_moe_forward, callable one at a time (for example
    to time each stage). lily_moe_forward runs exactly these kernels in this
-   order on the workspace. P = T * topk; rows 0..P-1 are the routed (token,
-   expert) pairs in expert order (row r = pair sorted_pairs[r]); rows
-   P..P+T-1 are the shared expert's rows for tokens 0..T-1.
+   order on the same workspace (layout under lily_moe_workspace_bytes).
+   P = T * topk; rows 0..P-1 are the routed (token, expert) pairs in expert
+   order (row r = pair sorted_pairs[r]); rows P..P+T-1 are the shared
+   expert's rows for tokens 0..T-1.
    lily_moe_gate_up: h[r] = bf16(silu(x Wg^T) * (x Wu^T)) with the weights
-     dequantised tile by tile on chip; h: bf16 bits [P + T, F].
-   lily_moe_down: y[r] = h[r] Wd^T in fp32; y: fp32 [P + T, H].
+     dequantised tile by tile on chip;
+   lily_moe_down: y[r] = h[r] Wd^T in fp32;
    lily_moe_combine: out[t] = bf16(y[P + t] + sum_j topk_w[t, j] *
      y[pair_rows[t * topk + j]]), fp32 sum in slot order; out: bf16 [T, H].
-   Errors as for lily_moe_forward (no workspace check). */
+   Errors as for lily_moe_forward. */
 int lily_moe_gate_up(const lily_moe_dims* dims, const lily_moe_weights* weights,
-                     const uint16_t* x, const lily_moe_routing* routing, uint16_t* h,
-                     void* stream);
-int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights, const uint16_t* h,
-                  const lily_moe_routing* routing, float* y, void* stream);
-int lily_moe_combine(const lily_moe_dims* dims, const float* y, const lily_moe_routing* routing,
-                     uint16_t* out, void* stream);
+                     const uint16_t* x, const lily_moe_routing* routing, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                  const lily_moe_routing* routing, void* workspace, size_t workspace_bytes,
+                  void* stream);
+int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
+                     void* workspace, size_t workspace_bytes, uint16_t* out, void* stream);
 
 /* Residual stream between stacked MoE layers (the pages describe a stack of
    layers but not this glue; the reading is a pre-norm residual with a

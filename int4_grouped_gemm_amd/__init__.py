@@ -26,7 +26,7 @@ LILY_ERR_HIP = -4
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
            "lily_w4_pack", "lily_moe_route", "lily_moe_forward", "lily_moe_gate_up",
            "lily_moe_down", "lily_moe_combine", "lily_residual_norm", "lily_last_error")
-LILY_SCHED_INTS = 32
+LILY_SCHED_INTS = 1056
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
 
@@ -91,13 +91,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                      ctypes.c_size_t, ctypes.c_void_p]
     lib.lily_moe_gate_up.restype = ctypes.c_int
     lib.lily_moe_gate_up.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
-                                     P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p]
+                                     P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]
     lib.lily_moe_down.restype = ctypes.c_int
-    lib.lily_moe_down.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
-                                  P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_moe_down.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), P(LilyMoeRouting),
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.lily_moe_combine.restype = ctypes.c_int
-    lib.lily_moe_combine.argtypes = [P(LilyMoeDims), ctypes.c_void_p, P(LilyMoeRouting),
-                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_moe_combine.argtypes = [P(LilyMoeDims), P(LilyMoeRouting), ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.lily_residual_norm.restype = ctypes.c_int
     lib.lily_residual_norm.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
@@ -235,25 +236,31 @@ def lily_moe_forward(d: LilyMoeDims, weights: Weights, x, routing: Routing, out,
     _check(rc, lib)
 
 
-def lily_moe_gate_up(d: LilyMoeDims, weights: Weights, x, routing: Routing, h,
+def _ws_bytes(workspace) -> int:
+    return workspace.numel() * workspace.element_size()
+
+
+def lily_moe_gate_up(d: LilyMoeDims, weights: Weights, x, routing: Routing, workspace,
                      stream=None) -> None:
     lib = load()
     rc = lib.lily_moe_gate_up(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(x),
-                              ctypes.byref(routing.c()), _ptr(h), _stream(stream))
-    _check(rc, lib)
-
-
-def lily_moe_down(d: LilyMoeDims, weights: Weights, h, routing: Routing, y, stream=None) -> None:
-    lib = load()
-    rc = lib.lily_moe_down(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(h),
-                           ctypes.byref(routing.c()), _ptr(y), _stream(stream))
-    _check(rc, lib)
-
-
-def lily_moe_combine(d: LilyMoeDims, y, routing: Routing, out, stream=None) -> None:
-    lib = load()
-    rc = lib.lily_moe_combine(ctypes.byref(d), _ptr(y), ctypes.byref(routing.c()), _ptr(out),
+                              ctypes.byref(routing.c()), _ptr(workspace), _ws_bytes(workspace),
                               _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_down(d: LilyMoeDims, weights: Weights, routing: Routing, workspace,
+                  stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_down(ctypes.byref(d), ctypes.byref(weights.c()), ctypes.byref(routing.c()),
+                           _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_combine(d: LilyMoeDims, routing: Routing, workspace, out, stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_combine(ctypes.byref(d), ctypes.byref(routing.c()), _ptr(workspace),
+                              _ws_bytes(workspace), _ptr(out), _stream(stream))
     _check(rc, lib)
 
 
@@ -291,7 +298,7 @@ def alloc_workspace(d: LilyMoeDims, device="cuda") -> torch.Tensor:
 def workspace_views(d: LilyMoeDims, ws: torch.Tensor):
     """(h, y) views of a forward workspace, laid out as the library uses it:
     h bf16 bits [P + T, F] at offset 0, y fp32 [P + T, H] at the next
-    256-byte boundary."""
+    256-byte boundary (the split-K partials, when present, follow y)."""
     rows = d.T * d.topk + d.T
     hb = rows * d.F * 2
     y0 = (hb + 255) // 256 * 256

@@ -26,15 +26,16 @@ int check_launch(const char* what) {
 int launch_route(const lily_moe_dims& d, const float* logits, const lily_moe_routing& r,
                  hipStream_t stream);
 int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
-                   const lily_moe_routing& r, int max_blocks, uint16_t* h, hipStream_t stream);
-int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* h,
-                const lily_moe_routing& r, int max_blocks, float* y, hipStream_t stream);
-int launch_combine(const lily_moe_dims& d, const float* y, const lily_moe_routing& r,
+                   const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
+                   hipStream_t stream);
+int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_moe_routing& r,
+                int max_blocks, const ForwardWorkspace& ws, hipStream_t stream);
+int launch_combine(const lily_moe_dims& d, const ForwardWorkspace& ws, const lily_moe_routing& r,
                    uint16_t* out, hipStream_t stream);
-size_t forward_workspace_bytes(const lily_moe_dims& d);
+size_t forward_workspace_bytes(const lily_moe_dims& d, int max_blocks);
+ForwardWorkspace forward_workspace_split(const lily_moe_dims& d, void* ws);
 size_t packed_w4_bytes(int n, int N, int K);
 int launch_pack(const lily_w4& w, int n, int N, int K, void* packed, hipStream_t stream);
-void forward_workspace_split(const lily_moe_dims& d, void* ws, uint16_t** h, float** y);
 int launch_residual_norm(int T, int H, float* r, const uint16_t* out, uint16_t* x_next,
                          float eps, hipStream_t stream);
 
@@ -131,6 +132,17 @@ static int check_forward_args(const lily_moe_dims* dims, const lily_moe_weights*
     return LILY_OK;
 }
 
+static int check_workspace(const lily_moe_dims& d, const void* workspace, size_t workspace_bytes) {
+    const size_t need = forward_workspace_bytes(d, max_blocks_of(d));
+    if (!workspace) return set_error(LILY_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned16(workspace))
+        return set_error(LILY_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+        return set_error(LILY_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+                         workspace_bytes, need);
+    return LILY_OK;
+}
+
 }  // namespace lily
 
 using namespace lily;
@@ -145,7 +157,7 @@ int32_t lily_moe_max_blocks(const lily_moe_dims* dims) {
 
 size_t lily_moe_workspace_bytes(const lily_moe_dims* dims) {
     if (check_dims(dims)) return 0;
-    return forward_workspace_bytes(*dims);
+    return forward_workspace_bytes(*dims, max_blocks_of(*dims));
 }
 
 size_t lily_w4_packed_bytes(int32_t n, int32_t N, int32_t K, int32_t group) {
@@ -182,54 +194,49 @@ int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
     if (rc) return rc;
     REQUIRE_PTR(x);
     REQUIRE_PTR(out);
-    const size_t need = forward_workspace_bytes(*dims);
-    if (!workspace) return set_error(LILY_ERR_INVALID_ARG, "workspace is NULL");
-    if (!aligned16(workspace))
-        return set_error(LILY_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    if (workspace_bytes < need)
-        return set_error(LILY_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
-                         workspace_bytes, need);
-    uint16_t* h;
-    float* y;
-    forward_workspace_split(*dims, workspace, &h, &y);
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    const ForwardWorkspace ws = forward_workspace_split(*dims, workspace);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int mb = max_blocks_of(*dims);
-    if ((rc = launch_gate_up(*dims, *weights, x, *routing, mb, h, s))) return rc;
-    if ((rc = launch_down(*dims, *weights, h, *routing, mb, y, s))) return rc;
-    return launch_combine(*dims, y, *routing, out, s);
+    if ((rc = launch_gate_up(*dims, *weights, x, *routing, mb, ws, s))) return rc;
+    if ((rc = launch_down(*dims, *weights, *routing, mb, ws, s))) return rc;
+    return launch_combine(*dims, ws, *routing, out, s);
 }
 
 int lily_moe_gate_up(const lily_moe_dims* dims, const lily_moe_weights* weights,
-                     const uint16_t* x, const lily_moe_routing* routing, uint16_t* h,
-                     void* stream) {
+                     const uint16_t* x, const lily_moe_routing* routing, void* workspace,
+                     size_t workspace_bytes, void* stream) {
     int rc = check_forward_args(dims, weights, routing);
     if (rc) return rc;
     REQUIRE_PTR(x);
-    REQUIRE_PTR(h);
-    return launch_gate_up(*dims, *weights, x, *routing, max_blocks_of(*dims), h,
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    return launch_gate_up(*dims, *weights, x, *routing, max_blocks_of(*dims),
+                          forward_workspace_split(*dims, workspace),
                           reinterpret_cast<hipStream_t>(stream));
 }
 
-int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights, const uint16_t* h,
-                  const lily_moe_routing* routing, float* y, void* stream) {
+int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                  const lily_moe_routing* routing, void* workspace, size_t workspace_bytes,
+                  void* stream) {
     int rc = check_forward_args(dims, weights, routing);
     if (rc) return rc;
-    REQUIRE_PTR(h);
-    REQUIRE_PTR(y);
-    return launch_down(*dims, *weights, h, *routing, max_blocks_of(*dims), y,
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    return launch_down(*dims, *weights, *routing, max_blocks_of(*dims),
+                       forward_workspace_split(*dims, workspace),
                        reinterpret_cast<hipStream_t>(stream));
 }
 
-int lily_moe_combine(const lily_moe_dims* dims, const float* y, const lily_moe_routing* routing,
-                     uint16_t* out, void* stream) {
+int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
+                     void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {
     int rc = check_dims(dims);
     if (rc) return rc;
     rc = check_routing(routing);
     if (rc) return rc;
-    REQUIRE_PTR(y);
     REQUIRE_PTR(out);
     if (dims->H % 4) return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 4", dims->H);
-    return launch_combine(*dims, y, *routing, out, reinterpret_cast<hipStream_t>(stream));
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    return launch_combine(*dims, forward_workspace_split(*dims, workspace), *routing, out,
+                          reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_residual_norm(int32_t T, int32_t H, float* r, const uint16_t* out, uint16_t* x_next,

@@ -12,7 +12,18 @@ constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kGroup = 64;     // weights per (scale, bias) group
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 64;
-constexpr int kSchedInts = LILY_SCHED_INTS;  // GEMM work-queue counters in a routing
+// The routing's sched array: 16 queue/finish counters per GEMM (gate/up,
+// down), then the split-K tile counters of each GEMM.
+constexpr int kSchedInts = LILY_SCHED_INTS;
+constexpr int kQueueInts = 32;
+constexpr int kTileCounters = (kSchedInts - kQueueInts) / 2;
+
+// Device buffers of the forward workspace.
+struct ForwardWorkspace {
+    uint16_t* h;  // bf16 [P + T, F]
+    float* y;     // fp32 [P + T, H]
+    float* part;  // split-K partial sums
+};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -30,6 +30,8 @@
 // 16-lane phase of a 16-byte read covers 256 bytes: rows r and r + 1 of one
 // chunk column already fall in different halves of the banks, and the
 // swizzle spreads each half's eight rows over its eight chunk slots.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace lily {
@@ -58,6 +60,13 @@ struct GemmArgs {
     int32_t* sched;     // kXcds queue counters, then the finished-workgroup counter
     uint16_t* h_out;    // gate/up: h [P + T, N] bf16
     float* y_out;       // down: y [P + T, N] fp32
+    // Split K (small block maps): each tile's K runs as kc items of K / kc;
+    // their fp32 partial sums go to part [kc][P + T][NP] (NP = 2N for
+    // gate/up: g then u; N for down) and the item that finishes a tile, as
+    // counted in tile_ctr [tiles], sums them in chunk order.
+    int kc;
+    float* part;
+    int32_t* tile_ctr;
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
@@ -212,6 +221,7 @@ struct Item {
     bool prefetched;         // its first NS - 1 stages are already in flight
     int r0, rows, n0;
     int mia;                 // 32-row sub-tiles that hold rows: min(MI, ceil(rows / 32))
+    int chunk, tile;         // K chunk of the item (split K) and its tile's counter index
     const char* a_base;      // A rows: + kt * 128
     uint32_t a_off[MI];      // row byte offset + swizzled chunk
     const char* w_base;
@@ -246,7 +256,7 @@ __device__ __forceinline__ void issue_stage(const Item<BM / 32>& it, int n_a, in
 // that the latency of its metadata loads overlaps the stores.
 template <int BM, bool GATED, int MIA, typename PrepNext>
 __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
-                                          const Item<BM / 32>& lp, uint32_t wave,
+                                          const Item<BM / 32>& lp, uint32_t wave, int* s_flag,
                                           PrepNext&& prep_next) {
     using Ld = Lds<BM>;
     constexpr int NS = Ld::NS;
@@ -257,7 +267,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
     const uint32_t smem = (uint32_t)(size_t)smem_p;  // LDS byte address
     const int lane = threadIdx.x % kWave;
     const int h = lane / 32;
-    const int nk = args.K / 64;
+    const int nk = args.K / 64 / args.kc;  // k-steps of this item (a_base, w_base start at its chunk)
     const int r0 = lp.r0, rows = lp.rows;
     int brow[2], col0[2];
 #pragma unroll
@@ -385,8 +395,61 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
 
     prep_next();
 
-    // Epilogue. C layout of a 32x32 tile: lane l, register r holds row
+    // C layout of a 32x32 tile: lane l, register r holds row
     // 8*(r/4) + 4*(l/32) + r%4 and column l%32.
+    if (args.kc > 1) {
+        // Split K: publish this chunk's partial sums; the item that
+        // completes the tile (the kc-th to arrive at its counter) adds all
+        // chunks in chunk order, so the result does not depend on which
+        // workgroup finishes last.
+        const int np = GATED ? 2 * args.N : args.N;
+        const size_t chunk_stride = (size_t)(args.P + args.T) * np;
+#pragma unroll
+        for (int i = 0; i < MIA; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+                if (row < rows) {
+                    float* prow = args.part + lp.chunk * chunk_stride + (size_t)(r0 + row) * np;
+#pragma unroll
+                    for (int g = 0; g < NI; ++g)
+                        __hip_atomic_store(prow + (GATED ? g * args.N + col0[0] : col0[g]) + lane % 32,
+                                           acc[i][g][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        // The partials are device-coherent stores (they write through the
+        // XCD's L2), complete before the barrier (__syncthreads waits for
+        // them), and read back with device-coherent loads: no fence, which on
+        // this GPU would write back the whole L2.
+        __syncthreads();
+        if (threadIdx.x == 0)
+            *s_flag = __hip_atomic_fetch_add(args.tile_ctr + lp.tile, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(*s_flag) != args.kc - 1) return;
+#pragma unroll
+        for (int i = 0; i < MIA; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+                if (row < rows) {
+                    const float* prow = args.part + (size_t)(r0 + row) * np;
+#pragma unroll
+                    for (int g = 0; g < NI; ++g) {
+                        const int col = (GATED ? g * args.N + col0[0] : col0[g]) + lane % 32;
+                        float sum = 0.0f;
+                        for (int c = 0; c < args.kc; ++c)
+                            sum += __hip_atomic_load(prow + c * chunk_stride + col, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                        acc[i][g][r] = sum;
+                    }
+                }
+            }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(args.tile_ctr + lp.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // Epilogue.
 #pragma unroll
     for (int i = 0; i < MIA; ++i) {
 #pragma unroll
@@ -412,7 +475,7 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
     constexpr int BN = GemmShape<GATED>::BN;
     constexpr int MI = BM / 32;
     __shared__ __attribute__((aligned(16))) char smem[Lds<BM>::TOTAL];
-    __shared__ int s_slot[2];
+    __shared__ int s_slot[3];  // two alternating queue slots, the split-K arrival count
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -430,9 +493,10 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
     int cq = blockIdx.x % kXcds;
     int tried = 0, toggle = 0;
 
-    // Items of queue q: its blocks q, q + 8, ... times the n-tiles.
+    // Items of queue q: its blocks q, q + 8, ... times the n-tiles times the
+    // K chunks (the chunks of a tile consecutive).
     auto items_of = [&](int q) {
-        return (nb_total > q ? (nb_total - q + kXcds - 1) / kXcds : 0) * n_tiles;
+        return (nb_total > q ? (nb_total - q + kXcds - 1) / kXcds : 0) * n_tiles * args.kc;
     };
     // Takes the next item of queue cq (one atomic) and resolves its rows,
     // expert and load plan; it.valid = false if the queue is empty.
@@ -442,8 +506,11 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
         const int c = grab(args.sched + cq, s_slot, toggle);
         if (c >= items_of(cq)) return;
         {
-            const int vb = cq + kXcds * (c / n_tiles);
-            const int nt = c % n_tiles;
+            const int ct = c / args.kc;  // tile of the queue
+            it.chunk = c - ct * args.kc;
+            const int vb = cq + kXcds * (ct / n_tiles);
+            const int nt = ct % n_tiles;
+            it.tile = vb * n_tiles + nt;
             int r_end, e = 0;
             bool shared;
             if (vb < args.shared_blocks) {
@@ -466,7 +533,8 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
             // swz(row, lane%8). Rows past the block read the block's first
             // row: their products land in output rows that are never
             // stored.
-            it.a_base = reinterpret_cast<const char*>(args.a);
+            const int kt0 = it.chunk * (args.K / 64 / args.kc);  // first k-step of the chunk
+            it.a_base = reinterpret_cast<const char*>(args.a) + kt0 * 128;
 #pragma unroll
             for (int j = 0; j < MI; ++j) {
                 const int row = 32 * j + 8 * (int)wave + lane / 8;
@@ -482,7 +550,7 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
             const int wb = (int)(wave >> 1);
             const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
             const int slab = GATED ? nt : 2 * nt + wb;
-            it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes;
+            it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes + (size_t)kt0 * kPackBlock;
             it.valid = true;
             return;
         }
@@ -513,17 +581,17 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
             if (nxt.valid) {
 #pragma unroll
                 for (int u = 0; u < Lds<BM>::NS - 1; ++u)
-                    if (u < args.K / 64) issue_stage<BM>(nxt, nxt.mia, u, u, smem_addr, wave, lane);
+                    if (u < args.K / 64 / args.kc) issue_stage<BM>(nxt, nxt.mia, u, u, smem_addr, wave, lane);
                 nxt.prefetched = true;
             }
         };
         // Only the 32-row sub-tiles that hold rows of the block are loaded
         // and multiplied.
         const int mia = cur.mia;
-        if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, cur, wave, prep);
-        else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, cur, wave, prep);
-        else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, cur, wave, prep);
-        else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, cur, wave, prep);
+        if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, cur, wave, s_slot + 2, prep);
+        else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, cur, wave, s_slot + 2, prep);
+        else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, cur, wave, s_slot + 2, prep);
+        else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, cur, wave, s_slot + 2, prep);
         steal(nxt);  // after the stores: only the last items of a workgroup get here with nothing
         cur = nxt;
     }
@@ -588,12 +656,54 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     }
 }
 
-// Workspace layout: h bf16 [P + T, F] then y fp32 [P + T, H], 256-byte aligned.
+// Workspace layout: h bf16 [P + T, F], then y fp32 [P + T, H], then (when a
+// GEMM splits K) the fp32 partial sums, each 256-byte aligned.
 static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t forward_workspace_bytes(const lily_moe_dims& d) {
+// Split K while the largest possible block map has few tiles: double the
+// chunk count while the items stay within kSplitItems and each chunk keeps
+// at least kSplitMinSteps k-steps. Depends on the sizes only, so that the
+// workspace size is known on the host.
+constexpr long kSplitItems = 1024;
+constexpr int kSplitMinSteps = 4;
+static_assert(kSplitItems / 2 <= kTileCounters, "split-K tile counters");
+
+static int split_k(const lily_moe_dims& d, int max_blocks, bool gated) {
+    const int BN = gated ? 128 : 256;
+    const int N = gated ? d.F : d.H;
+    const int nk = (gated ? d.H : d.F) / 64;
+    const long tiles = (long)(max_blocks + (d.T + d.tile_m - 1) / d.tile_m) * (N / BN);
+    int kc = 1;
+    while (nk % (2 * kc) == 0 && nk / (2 * kc) >= kSplitMinSteps && tiles * 2 * kc <= kSplitItems)
+        kc *= 2;
+    return kc;
+}
+
+static size_t part_bytes(const lily_moe_dims& d, int max_blocks) {
     const size_t rows = (size_t)d.T * d.topk + d.T;
-    return align_up(rows * d.F * sizeof(uint16_t)) + align_up(rows * d.H * sizeof(float));
+    const int kg = split_k(d, max_blocks, true), kd = split_k(d, max_blocks, false);
+    size_t b = 0;
+    if (kg > 1) b = (size_t)kg * rows * 2 * d.F * sizeof(float);
+    if (kd > 1) b = std::max(b, (size_t)kd * rows * d.H * sizeof(float));
+    return b;
+}
+
+size_t forward_workspace_bytes(const lily_moe_dims& d, int max_blocks) {
+    const size_t rows = (size_t)d.T * d.topk + d.T;
+    return align_up(rows * d.F * sizeof(uint16_t)) + align_up(rows * d.H * sizeof(float)) +
+           align_up(part_bytes(d, max_blocks));
+}
+
+ForwardWorkspace forward_workspace_split(const lily_moe_dims& d, void* ws) {
+    const size_t rows = (size_t)d.T * d.topk + d.T;
+    char* p = reinterpret_cast<char*>(ws);
+    ForwardWorkspace w;
+    w.h = reinterpret_cast<uint16_t*>(p);
+    p += align_up(rows * d.F * sizeof(uint16_t));
+    w.y = reinterpret_cast<float*>(p);
+    p += align_up(rows * d.H * sizeof(float));
+    w.part = reinterpret_cast<float*>(p);
+    return w;
 }
 
 static GemmArgs routing_args(const lily_moe_dims& d, const lily_moe_routing& r) {
@@ -611,7 +721,7 @@ static GemmArgs routing_args(const lily_moe_dims& d, const lily_moe_routing& r) 
 
 // Persistent grid: the workgroups that fit on the device at once (from the
 // kernel's own occupancy), fewer if the largest possible block map has
-// fewer tiles, a multiple of the queue count.
+// fewer items (tiles times K chunks), a multiple of the queue count.
 template <int BM, bool GATED>
 static int gemm_grid(GemmArgs& g, int max_blocks) {
     constexpr int kMaxDevices = 64;
@@ -630,8 +740,8 @@ static int gemm_grid(GemmArgs& g, int max_blocks) {
         if (dev < kMaxDevices) resident[dev] = slots;
     }
     g.shared_blocks = (g.T + BM - 1) / BM;
-    const long tiles = (long)(max_blocks + g.shared_blocks) * (g.N / GemmShape<GATED>::BN);
-    const long grid = tiles < slots ? tiles : slots;
+    const long items = (long)(max_blocks + g.shared_blocks) * (g.N / GemmShape<GATED>::BN) * g.kc;
+    const long grid = items < slots ? items : slots;
     return (int)((grid + kXcds - 1) / kXcds * kXcds);
 }
 
@@ -651,7 +761,8 @@ static int launch_down_bm(GemmArgs g, int max_blocks, hipStream_t stream) {
 
 // G1 + G2 (and the shared expert's rows): h = bf16(silu(x Wg^T) * (x Wu^T)).
 int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
-                   const lily_moe_routing& r, int max_blocks, uint16_t* h, hipStream_t stream) {
+                   const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
+                   hipStream_t stream) {
     GemmArgs g = routing_args(d, r);
     g.a = x;
     g.sorted_pairs = r.sorted_pairs;
@@ -662,7 +773,10 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
     g.N = d.F;
     g.K = d.H;
     g.sched = r.sched;
-    g.h_out = h;
+    g.h_out = ws.h;
+    g.kc = split_k(d, max_blocks, true);
+    g.part = ws.part;
+    g.tile_ctr = r.sched + kQueueInts;
     switch (d.tile_m) {
         case 32: return launch_gate_up_bm<32>(g, max_blocks, stream);
         case 64: return launch_gate_up_bm<64>(g, max_blocks, stream);
@@ -672,16 +786,19 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
 }
 
 // G3 (and the shared expert's rows): y = h Wd^T in fp32.
-int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* h,
-                const lily_moe_routing& r, int max_blocks, float* y, hipStream_t stream) {
+int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_moe_routing& r,
+                int max_blocks, const ForwardWorkspace& ws, hipStream_t stream) {
     GemmArgs g = routing_args(d, r);
-    g.a = h;
+    g.a = ws.h;
     g.w[0] = g.w[1] = static_cast<const char*>(w.down);
     g.sw[0] = g.sw[1] = static_cast<const char*>(w.sh_down);
     g.N = d.H;
     g.K = d.F;
-    g.sched = r.sched + LILY_SCHED_INTS / 2;
-    g.y_out = y;
+    g.sched = r.sched + kQueueInts / 2;
+    g.y_out = ws.y;
+    g.kc = split_k(d, max_blocks, false);
+    g.part = ws.part;
+    g.tile_ctr = r.sched + kQueueInts + kTileCounters;
     switch (d.tile_m) {
         case 32: return launch_down_bm<32>(g, max_blocks, stream);
         case 64: return launch_down_bm<64>(g, max_blocks, stream);
@@ -703,18 +820,13 @@ int launch_pack(const lily_w4& w, int n, int N, int K, void* packed, hipStream_t
 }
 
 // G5: weighted gather-combine.
-int launch_combine(const lily_moe_dims& d, const float* y, const lily_moe_routing& r,
+int launch_combine(const lily_moe_dims& d, const ForwardWorkspace& ws, const lily_moe_routing& r,
                    uint16_t* out, hipStream_t stream) {
+    const float* y = ws.y;
     hipLaunchKernelGGL(combine_kernel, dim3(d.T), dim3(256), 0, stream, y, r.pair_rows, r.topk_w,
                        d.T * d.topk, d.H, d.topk, out);
     return check_launch("combine");
 }
 
-void forward_workspace_split(const lily_moe_dims& d, void* ws, uint16_t** h, float** y) {
-    const size_t rows = (size_t)d.T * d.topk + d.T;
-    *h = reinterpret_cast<uint16_t*>(ws);
-    *y = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                  align_up(rows * d.F * sizeof(uint16_t)));
-}
 
 }  // namespace lily

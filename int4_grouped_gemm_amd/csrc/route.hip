@@ -285,7 +285,7 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
             s_bst[E] = tot_blks;
         }
     }
-    if (tid < kSchedInts) sched[tid] = 0;
+    for (int i = tid; i < kSchedInts; i += kFinishThreads) sched[i] = 0;
     __syncthreads();
 
     for (int e = tid; e <= E; e += kFinishThreads) offsets[e] = s_off[e];

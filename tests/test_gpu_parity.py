@@ -175,14 +175,45 @@ def test_gemm_queue_counters_reset():
     r = G.route_gpu(d, S.router_logits(cfg))
     ws = L.alloc_workspace(d)
     h, y = L.workspace_views(d, ws)
-    L.lily_moe_gate_up(d, w, xd, r, h)
+    L.lily_moe_gate_up(d, w, xd, r, ws)
     torch.cuda.synchronize()
     first = h.clone()
     assert not np.any(r.sched.cpu().numpy())
     h.fill_(0)
-    L.lily_moe_gate_up(d, w, xd, r, h)
-    L.lily_moe_down(d, w, h, r, y)
-    L.lily_moe_down(d, w, h, r, y)
+    L.lily_moe_gate_up(d, w, xd, r, ws)
+    L.lily_moe_down(d, w, r, ws)
+    L.lily_moe_down(d, w, r, ws)
     torch.cuda.synchronize()
     assert torch.equal(first, h)
     assert not np.any(r.sched.cpu().numpy())
+
+
+# ------------------------------------------------------------------- split K
+
+@pytest.mark.parametrize("T,tile_m", [(1, 32), (1, 128), (4, 32), (8, 64), (3, 128)])
+def test_forward_small_T_split_k(T, tile_m):
+    """Few tokens: the GEMMs spread each tile's K over several workgroups and
+    the last to finish adds the fp32 partials in chunk order. All tokens
+    against the oracle, twice (deterministic), then twice more on the same
+    routing (the tile counters are left zero)."""
+    cfg = S.CONFIGS["prefill512"]
+    _flush(f"small T: T={T} tile_m={tile_m}")
+    lw = S.layer_weights(cfg, 0)
+    x = S.activations(cfg, 0, T=T)
+    lg = S.router_logits(cfg, 0, 0, T=T)
+    d = L.dims(T, cfg.H, cfg.F, cfg.E, cfg.k, tile_m)
+    w = L.weights_from_host(lw)
+    r = G.route_gpu(d, lg)
+    ref_r = oracle.route(lg, cfg.k, tile_m)
+    G.compare_routing(G.routing_to_host(r), ref_r, tile_m)
+    xd = G.to_dev_bits(x)
+    got = G.from_dev_bits(G.forward_gpu(d, w, xd, r))
+    acc, _ = oracle.forward(x, ref_r["topk_ids"], ref_r["topk_w"], oracle.getter_from_layer(lw),
+                            cfg.H, cfg.F, cfg.E)
+    err = G.output_error(got, acc)
+    _flush(f"  normalised error {err:.4f}")
+    assert err <= 1.0, f"normalised error {err}"
+    for _ in range(2):
+        again = G.from_dev_bits(G.forward_gpu(d, w, xd, r))
+        assert np.array_equal(again, got), "split-K forward is not deterministic"
+    assert not np.any(r.sched.cpu().numpy()), "tile counters must be left zero"
