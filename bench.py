@@ -47,6 +47,8 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "decode40"],
+                    help="prefill2048_zipf (the headline) or decode40 (T=1, 40-layer steps)")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer weight sets cycled")
@@ -78,6 +80,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the layer is a single-GPU kernel path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "decode40":
+        return main_decode(args)
 
     import numpy as np
     import torch
@@ -220,6 +225,71 @@ def main():
             "sample": f"route of all {cfg.T} tokens + forward of {ntok} tokens of layer 0 "
                       f"(dequant of the experts they use included), {c1 - c0:.1f} s",
         }
+    print(json.dumps(result), flush=True)
+
+
+def main_decode(args):
+    """Batch-1 decode: one step = 40 MoE layers at T = 1 (route + forward per
+    layer). The 40 layers cycle through --layers distinct weight sets (8 by
+    default, 3.6 GB), so every layer's weights stream from HBM. Each step and
+    layer has its own router logits; all inputs are resident before timing."""
+    import numpy as np
+    import torch
+
+    import int4_grouped_gemm_amd as L
+    from synth import inputs as S
+
+    L.load()
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS["decode40"]
+    n_layers = cfg.layers
+    d = L.dims(1, cfg.H, cfg.F, cfg.E, cfg.k, 32)
+    weights = [L.weights_from_host(S.layer_weights(cfg, layer), dev) for layer in range(args.layers)]
+    n_steps = args.warmup + args.steps
+    logits = torch.from_numpy(np.stack([np.stack([S.router_logits(cfg, layer, step % cfg.steps)
+                                                  for layer in range(n_layers)])
+                                        for step in range(n_steps)])).to(dev)
+    xs = torch.from_numpy(np.stack([S.activations(cfg, step % cfg.steps).view(np.int16)
+                                    for step in range(n_steps)])).to(dev)
+    routing = L.alloc_routing(d, dev)
+    ws = L.alloc_workspace(d, dev)
+    out = torch.empty((1, cfg.H), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        for layer in range(n_layers):
+            L.lily_moe_route(d, logits[i, layer], routing, stream)
+            L.lily_moe_forward(d, weights[layer % args.layers], xs[i], routing, out, ws,
+                               stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    us_per_layer = ms_per_step * 1e3 / n_layers
+    # weight bytes a layer must read: the k routed experts and the shared one
+    layer_bytes = (cfg.k + 1) * 3 * cfg.H * cfg.F * (0.5 + 4.0 / 64)
+    gbs = layer_bytes / (us_per_layer * 1e-6) / 1e9
+    result = {
+        "metric": "MoE-layer decode time per layer (T=1, 40-layer step, int4 g64); % of HBM peak",
+        "value": round(us_per_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode40", "T": 1, "H": cfg.H, "F": cfg.F, "E": cfg.E,
+                   "topk": cfg.k, "layers_per_step": n_layers, "layer_weight_sets": args.layers,
+                   "tile_m": 32},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "whole layer (route + gate_up + down + combine)"},
+    }
     print(json.dumps(result), flush=True)
 
 
