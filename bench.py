@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer weight sets cycled")
     ap.add_argument("--tile-m", type=int, default=128)
+    ap.add_argument("--decode-path", default="fused", choices=["fused", "layer"],
+                    help="decode40: lily_moe_decode (one launch per layer) or route + forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of layer 0 the CPU oracle computes for the baseline")
@@ -258,9 +260,12 @@ def main_decode(args):
 
     def step(i):
         for layer in range(n_layers):
-            L.lily_moe_route(d, logits[i, layer], routing, stream)
-            L.lily_moe_forward(d, weights[layer % args.layers], xs[i], routing, out, ws,
-                               stream=stream)
+            w = weights[layer % args.layers]
+            if args.decode_path == "fused":
+                L.lily_moe_decode(d, w, logits[i, layer], xs[i], routing, out, ws, stream)
+            else:
+                L.lily_moe_route(d, logits[i, layer], routing, stream)
+                L.lily_moe_forward(d, w, xs[i], routing, out, ws, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -285,10 +290,11 @@ def main_decode(args):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode40", "T": 1, "H": cfg.H, "F": cfg.F, "E": cfg.E,
                    "topk": cfg.k, "layers_per_step": n_layers, "layer_weight_sets": args.layers,
-                   "tile_m": 32},
+                   "path": "lily_moe_decode" if args.decode_path == "fused"
+                   else "lily_moe_route + lily_moe_forward (tile_m 32)"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "whole layer (route + gate_up + down + combine)"},
+                     "kernel": "whole layer"},
     }
     print(json.dumps(result), flush=True)
 

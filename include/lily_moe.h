@@ -216,6 +216,24 @@ int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
 int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
                      void* workspace, size_t workspace_bytes, uint16_t* out, void* stream);
 
+/* Route and forward of one MoE layer for a few tokens (T <= 4, decode) in
+   one launch: the same result as lily_moe_route then lily_moe_forward, up to
+   fp32 summation order. Every weight of the k routed experts and of the
+   shared expert is read once, spread over all compute units as
+   matrix-vector products; three phases (gate/up, down, combine) are
+   separated by device-wide barriers of a cooperative launch.
+   logits fp32 [T, E], x bf16 [T, H]; out bf16 [T, H]. Of the routing only
+   topk_ids, topk_w (written) and sched (sched[28..29] are the barrier's
+   counters, zero on entry and left zero; sched[30] is set to 1 if a barrier
+   wait gave up after about a second, which makes out invalid) are used.
+   Needs H a multiple of 512 (at most 8192), F a multiple of 128 (at most
+   4096). workspace: lily_moe_workspace_bytes(dims) bytes.
+   Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (T > 4, sizes),
+   LILY_ERR_WORKSPACE, LILY_ERR_HIP (including a failed cooperative launch). */
+int lily_moe_decode(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                    const float* logits, const uint16_t* x, const lily_moe_routing* routing,
+                    uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Residual stream between stacked MoE layers (the pages describe a stack of
    layers but not this glue; the reading is a pre-norm residual with a
    unit-gain RMSNorm): r += out (fp32), then

@@ -25,7 +25,8 @@ LILY_ERR_HIP = -4
 
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
            "lily_w4_pack", "lily_moe_route", "lily_moe_forward", "lily_moe_gate_up",
-           "lily_moe_down", "lily_moe_combine", "lily_residual_norm", "lily_last_error")
+           "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_residual_norm",
+           "lily_last_error")
 LILY_SCHED_INTS = 1056
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
@@ -99,6 +100,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_moe_combine.restype = ctypes.c_int
     lib.lily_moe_combine.argtypes = [P(LilyMoeDims), P(LilyMoeRouting), ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_moe_decode.restype = ctypes.c_int
+    lib.lily_moe_decode.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
+                                    ctypes.c_void_p, P(LilyMoeRouting), ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.lily_residual_norm.restype = ctypes.c_int
     lib.lily_residual_norm.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
@@ -261,6 +266,16 @@ def lily_moe_combine(d: LilyMoeDims, routing: Routing, workspace, out, stream=No
     lib = load()
     rc = lib.lily_moe_combine(ctypes.byref(d), ctypes.byref(routing.c()), _ptr(workspace),
                               _ws_bytes(workspace), _ptr(out), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_decode(d: LilyMoeDims, weights: Weights, logits, x, routing: Routing, out, workspace,
+                    stream=None) -> None:
+    """Route + forward of a few tokens (T <= 4) in one launch."""
+    lib = load()
+    rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(logits), _ptr(x),
+                             ctypes.byref(routing.c()), _ptr(out), _ptr(workspace),
+                             _ws_bytes(workspace), _stream(stream))
     _check(rc, lib)
 
 

@@ -36,6 +36,10 @@ size_t forward_workspace_bytes(const lily_moe_dims& d, int max_blocks);
 ForwardWorkspace forward_workspace_split(const lily_moe_dims& d, void* ws);
 size_t packed_w4_bytes(int n, int N, int K);
 int launch_pack(const lily_w4& w, int n, int N, int K, void* packed, hipStream_t stream);
+int decode_supported(const lily_moe_dims& d);
+int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float* logits,
+                  const uint16_t* x, const lily_moe_routing& r, uint16_t* out, void* workspace,
+                  hipStream_t stream);
 int launch_residual_norm(int T, int H, float* r, const uint16_t* out, uint16_t* x_next,
                          float eps, hipStream_t stream);
 
@@ -237,6 +241,31 @@ int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
     if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
     return launch_combine(*dims, forward_workspace_split(*dims, workspace), *routing, out,
                           reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_decode(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                    const float* logits, const uint16_t* x, const lily_moe_routing* routing,
+                    uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if ((rc = decode_supported(*dims))) return rc;
+    if (!weights) return set_error(LILY_ERR_INVALID_ARG, "weights is NULL");
+    if ((rc = check_packed(weights->gate, "gate")) || (rc = check_packed(weights->up, "up")) ||
+        (rc = check_packed(weights->down, "down")) ||
+        (rc = check_packed(weights->sh_gate, "sh_gate")) ||
+        (rc = check_packed(weights->sh_up, "sh_up")) ||
+        (rc = check_packed(weights->sh_down, "sh_down")))
+        return rc;
+    if (!routing) return set_error(LILY_ERR_INVALID_ARG, "routing is NULL");
+    REQUIRE_PTR(routing->topk_ids);
+    REQUIRE_PTR(routing->topk_w);
+    REQUIRE_PTR(routing->sched);
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(out);
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    return launch_decode(*dims, *weights, logits, x, *routing, out, workspace,
+                         reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_residual_norm(int32_t T, int32_t H, float* r, const uint16_t* out, uint16_t* x_next,

@@ -17,6 +17,9 @@ constexpr int kMaxTopk = 64;
 constexpr int kSchedInts = LILY_SCHED_INTS;
 constexpr int kQueueInts = 32;
 constexpr int kTileCounters = (kSchedInts - kQueueInts) / 2;
+// sched[28], sched[29]: the fused decode kernel's device-wide barrier
+// (arrivals, exits); sched[30]: set if one of its barrier waits gave up.
+constexpr int kDecodeBarrier = 28;
 
 // Device buffers of the forward workspace.
 struct ForwardWorkspace {
@@ -46,11 +49,21 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
+// A wave-uniform pointer, made explicit so that it lives in SGPRs.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Host-side launch bookkeeping shared by the sources.
 struct LaunchError {
     int code;
     const char* what;
 };
+
+size_t decode_workspace_bytes(const lily_moe_dims& d);  // 0 when T is too large
 
 // Records the thread's last error text; returns code.
 int set_error(int code, const char* fmt, ...);

@@ -33,15 +33,9 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "w4.hpp"
 
 namespace lily {
-
-// Packed weight layout (lily_w4_pack): one block per (expert, 128-row slab,
-// group of 64 k); q as [2 halves][128 rows][16 bytes], then the 128 scales,
-// then the 128 biases.
-constexpr int kPackRows = 128;
-constexpr int kPackQ = 4096;
-constexpr int kPackBlock = 4608;
 
 struct GemmArgs {
     const uint16_t* a;              // A rows: gate/up -> x [T, K]; down -> h [P + T, K]
@@ -70,32 +64,6 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
-// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (a few ulp
-// of fp32, far below the bf16 rounding of h that follows).
-__device__ __forceinline__ float silu(float z) {
-    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
-}
-
-// Eight int4 weights (one 32-bit word: element 2i in the low nibble of byte
-// i) -> four bf16x2 words of w = bf16(scale * q + bias), elements in order.
-// A byte 0x00..0x0F read as an OCP e4m3 value is exactly q * 2^-9 (exponent
-// field 0 or 1), so one v_cvt_pk_f32_fp8 widens two nibbles, and with
-// s512 = scale * 2^9 (exact) fma(s512, q * 2^-9, bias) is the same single
-// rounding of scale * q + bias as fma(scale, q, bias).
-__device__ __forceinline__ void dequant8(uint32_t v, float s512, float b, uint32_t out[4]) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    const uint32_t lo = v & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
-    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
-    const f2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const f2 e46 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const f2 e13 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const f2 e57 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    out[0] = pack_bf16x2(fmaf(s512, e02[0], b), fmaf(s512, e13[0], b));
-    out[1] = pack_bf16x2(fmaf(s512, e02[1], b), fmaf(s512, e13[1], b));
-    out[2] = pack_bf16x2(fmaf(s512, e46[0], b), fmaf(s512, e57[0], b));
-    out[3] = pack_bf16x2(fmaf(s512, e46[1], b), fmaf(s512, e57[1], b));
-}
 
 // Tile geometry. A workgroup has 4 wavefronts that split the output columns;
 // every wavefront covers all BM rows of the block. The workgroup owns 256
@@ -174,14 +142,6 @@ __device__ __forceinline__ void barrier_only() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// A wave-uniform pointer, made explicit so that it lives in SGPRs.
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Global -> LDS load (gfx950 LDS DMA) with a wave-uniform 64-bit base in
@@ -690,8 +650,9 @@ static size_t part_bytes(const lily_moe_dims& d, int max_blocks) {
 
 size_t forward_workspace_bytes(const lily_moe_dims& d, int max_blocks) {
     const size_t rows = (size_t)d.T * d.topk + d.T;
-    return align_up(rows * d.F * sizeof(uint16_t)) + align_up(rows * d.H * sizeof(float)) +
-           align_up(part_bytes(d, max_blocks));
+    const size_t fwd = align_up(rows * d.F * sizeof(uint16_t)) + align_up(rows * d.H * sizeof(float)) +
+                       align_up(part_bytes(d, max_blocks));
+    return std::max(fwd, decode_workspace_bytes(d));  // lily_moe_decode uses the same workspace
 }
 
 ForwardWorkspace forward_workspace_split(const lily_moe_dims& d, void* ws) {

@@ -29,6 +29,7 @@
 //                 their work-queue counters.
 // For small T the top-k runs inside route_finish and the route is one launch.
 #include "common.hpp"
+#include "topk.hpp"
 
 namespace lily {
 
@@ -37,95 +38,10 @@ constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kTopkThreads = 256;
 constexpr int kTopkTokensPerWave = 1;
 constexpr int kTopkTokensPerBlock = (kTopkThreads / kWave) * kTopkTokensPerWave;
-constexpr int kMaxPerLane = kMaxExperts / kWave;
 // Up to this many tokens the whole route runs in the single workgroup.
 constexpr int kFusedRouteMaxT = 64;
 // Chunks of 64 ids a wavefront loads at once in route_finish.
 constexpr int kBatch = 16;
-
-// Order-preserving map of a float to uint32; -0.0 is folded onto +0.0 so
-// that the two tie.
-__device__ __forceinline__ uint32_t ordered_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
-    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-    return __uint_as_float(u);
-}
-
-// Maximum of a uint32 over the 64 lanes, returned uniformly: DPP within each
-// row of 16 lanes (quad swaps, then rotations by 4 and 8), then the four row
-// results through readlane. No LDS traffic.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false)); // row_ror 4
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false)); // row_ror 8
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-    return max(max(a, b), max(c, d));
-}
-
-// Top-k and softmax of one token by one wavefront. Lane l holds the logits
-// of experts l, l + 64, ... as order-preserving keys; a taken expert's key
-// becomes 0, below every real key. Each round takes the wavefront maximum
-// and, among the experts holding it, the lowest index (ballots in expert
-// order).
-__device__ __forceinline__ void topk_one_token(const float* __restrict__ logits, int t, int E,
-                                               int k, int32_t* __restrict__ topk_ids,
-                                               float* __restrict__ topk_w) {
-    const int lane = threadIdx.x % kWave;
-    const float* row = logits + (size_t)t * E;
-    const int nper = (E + kWave - 1) / kWave;
-    uint32_t key[kMaxPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + i * kWave;
-        key[i] = (i < nper && e < E) ? ordered_bits(row[e]) : 0u;
-    }
-    int my_id = 0;
-    float my_l = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        uint32_t best = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (i < nper) best = max(best, key[i]);
-        best = wave_max_u32(best);
-        int e_sel = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            if (i >= nper) break;
-            const uint64_t hit = __ballot(key[i] == best);
-            if (hit) {
-                e_sel = i * kWave + (int)__ffsll((long long)hit) - 1;
-                break;
-            }
-        }
-        if (lane == e_sel % kWave) {
-#pragma unroll
-            for (int i = 0; i < kMaxPerLane; ++i)
-                if (i == e_sel / kWave) key[i] = 0u;
-        }
-        if (lane == j) {
-            my_id = e_sel;
-            my_l = from_ordered_bits(best);
-        }
-    }
-    // softmax over the selected logits, summed in slot order
-    const float l0 = __shfl(my_l, 0, kWave);
-    const float ex = expf(my_l - l0);
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
-    if (lane < k) {
-        topk_ids[(size_t)t * k + lane] = my_id;
-        topk_w[(size_t)t * k + lane] = ex / sum;
-    }
-}
 
 __global__ void __launch_bounds__(kTopkThreads) route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_ids,

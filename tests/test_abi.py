@@ -163,3 +163,26 @@ def test_pack_rejects(lib):
     bad = L.LilyW4(FAKE, FAKE + 2, FAKE)
     assert pack(ctypes.byref(bad), 1, 128, 64, 64, FAKE, None) == L.LILY_ERR_INVALID_ARG
     assert "scale" in lib.lily_last_error().decode()
+
+
+def test_decode_rejects(lib):
+    d = good_dims(T=5, H=512, F=128)
+    rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights()), FAKE, FAKE,
+                             ctypes.byref(routing()), FAKE, FAKE, 1 << 40, None)
+    assert rc == L.LILY_ERR_UNSUPPORTED and "T = 5" in lib.lily_last_error().decode()
+    d = good_dims(T=1, H=256, F=128)
+    rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights()), FAKE, FAKE,
+                             ctypes.byref(routing()), FAKE, FAKE, 1 << 40, None)
+    assert rc == L.LILY_ERR_UNSUPPORTED and "H = 256" in lib.lily_last_error().decode()
+    d = good_dims(T=1, H=512, F=128)
+    rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights()), FAKE, FAKE,
+                             ctypes.byref(routing()), FAKE, FAKE, 1 << 40, None)
+    assert rc == L.LILY_ERR_UNSUPPORTED and "F = 128" in lib.lily_last_error().decode()
+    d = good_dims(T=1, H=512, F=256)
+    rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights()), None, FAKE,
+                             ctypes.byref(routing()), FAKE, FAKE, 1 << 40, None)
+    assert rc == L.LILY_ERR_INVALID_ARG and "logits" in lib.lily_last_error().decode()
+    need = lib.lily_moe_workspace_bytes(ctypes.byref(d))
+    rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights()), FAKE, FAKE,
+                             ctypes.byref(routing()), FAKE, FAKE, need - 1, None)
+    assert rc == L.LILY_ERR_WORKSPACE

@@ -217,3 +217,42 @@ def test_forward_small_T_split_k(T, tile_m):
         again = G.from_dev_bits(G.forward_gpu(d, w, xd, r))
         assert np.array_equal(again, got), "split-K forward is not deterministic"
     assert not np.any(r.sched.cpu().numpy()), "tile counters must be left zero"
+
+
+# ------------------------------------------------------------------- fused decode
+
+@pytest.mark.parametrize("name,T", [("decode40", 1), ("prefill512", 2), ("prefill512", 4),
+                                    ("prefill2048_zipf", 3)])
+def test_decode_fused(name, T):
+    """lily_moe_decode (route and forward in one cooperative launch) against
+    the oracle: top-k ids exact, weights within 2e-6, outputs within the
+    tolerance; run twice bit-identically; barrier counters left zero."""
+    cfg = S.CONFIGS[name]
+    _flush(f"fused decode {name} T={T}")
+    lw = S.layer_weights(cfg, 0)
+    x = S.activations(cfg, 0, T=T)
+    lg = S.router_logits(cfg, 0, 0, T=T)
+    d = L.dims(T, cfg.H, cfg.F, cfg.E, cfg.k, 32)
+    w = L.weights_from_host(lw)
+    r = L.alloc_routing(d)
+    ws = L.alloc_workspace(d)
+    ws.fill_(0xFF)
+    lgd = torch.from_numpy(lg).cuda()
+    xd = G.to_dev_bits(x)
+    out = torch.full((T, cfg.H), -1, dtype=torch.int16, device="cuda")
+    L.lily_moe_decode(d, w, lgd, xd, r, out, ws)
+    torch.cuda.synchronize()
+    ref_r = oracle.route(lg, cfg.k, 32)
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ref_r["topk_ids"])
+    assert np.max(np.abs(r.topk_w.cpu().numpy() - ref_r["topk_w"])) <= 2e-6
+    got = G.from_dev_bits(out)
+    acc, _ = oracle.forward(x, ref_r["topk_ids"], ref_r["topk_w"], oracle.getter_from_layer(lw),
+                            cfg.H, cfg.F, cfg.E)
+    err = G.output_error(got, acc)
+    _flush(f"  normalised error {err:.4f}")
+    assert err <= 1.0, f"normalised error {err}"
+    again = torch.full_like(out, -1)
+    L.lily_moe_decode(d, w, lgd, xd, r, again, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out), "fused decode is not deterministic"
+    assert not np.any(r.sched.cpu().numpy()), "barrier counters and error flag must be zero"

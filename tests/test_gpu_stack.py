@@ -38,9 +38,10 @@ def _gpu():
     L.load()
 
 
-def run_chain(cfg, chunks, sample, tile_m=128, n_layers=None):
+def run_chain(cfg, chunks, sample, tile_m=128, n_layers=None, fused_decode=False):
     """chunks: list of chunk indices (prefill chunk or decode step); sample:
-    token indices inside each chunk that the oracle follows."""
+    token indices inside each chunk that the oracle follows. fused_decode:
+    run each layer with lily_moe_decode instead of route + forward."""
     dev = torch.device("cuda")
     n_layers = n_layers or cfg.layers
     T = cfg.T
@@ -69,11 +70,18 @@ def run_chain(cfg, chunks, sample, tile_m=128, n_layers=None):
         for ci, c in enumerate(chunks):
             lg = S.router_logits(cfg, layer, c)
             ref_r = oracle.route(lg, cfg.k, tile_m)
-            L.lily_moe_route(d, torch.from_numpy(lg).to(dev), rt)
-            L.lily_moe_forward(d, w, gpu_x[ci], rt, out, ws)
+            if fused_decode:
+                L.lily_moe_decode(d, w, torch.from_numpy(lg).to(dev), gpu_x[ci], rt, out, ws)
+            else:
+                L.lily_moe_route(d, torch.from_numpy(lg).to(dev), rt)
+                L.lily_moe_forward(d, w, gpu_x[ci], rt, out, ws)
             L.lily_residual_norm(T, cfg.H, gpu_r[ci], out, gpu_x[ci], EPS)
             torch.cuda.synchronize()
-            G.compare_routing(G.routing_to_host(rt), ref_r, tile_m)
+            if fused_decode:
+                assert np.array_equal(rt.topk_ids.cpu().numpy(), ref_r["topk_ids"])
+                assert not np.any(rt.sched.cpu().numpy())
+            else:
+                G.compare_routing(G.routing_to_host(rt), ref_r, tile_m)
             ids_s.append(ref_r["topk_ids"][sample])
             wts_s.append(ref_r["topk_w"][sample])
             got.append(G.from_dev_bits(out)[sample])
@@ -97,9 +105,10 @@ def test_stack40_T8192_chunked():
     _flush(f"  worst normalised error over 40 layers: {worst:.4f}")
 
 
-def test_decode40_steps():
+@pytest.mark.parametrize("fused", [False, True], ids=["route_forward", "fused_decode"])
+def test_decode40_steps(fused):
     cfg = S.CONFIGS["decode40"]
     steps = [0, 1, 128, 255]
-    _flush(f"decode: {cfg.layers} layers, T=1, steps {steps} of {cfg.steps}")
-    worst = run_chain(cfg, steps, [0])
+    _flush(f"decode: {cfg.layers} layers, T=1, steps {steps} of {cfg.steps}, fused={fused}")
+    worst = run_chain(cfg, steps, [0], fused_decode=fused)
     _flush(f"  worst normalised error over 40 layers: {worst:.4f}")
