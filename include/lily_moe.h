@@ -217,19 +217,27 @@ int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
                      void* workspace, size_t workspace_bytes, uint16_t* out, void* stream);
 
 /* Route and forward of one MoE layer for a few tokens (T <= 4, decode) in
-   one launch: the same result as lily_moe_route then lily_moe_forward, up to
-   fp32 summation order. Every weight of the k routed experts and of the
-   shared expert is read once, spread over all compute units as
-   matrix-vector products; three phases (gate/up, down, combine) are
-   separated by device-wide barriers of a cooperative launch.
+   one launch: the routing of lily_moe_route (same ids and weights) and the
+   output of lily_moe_forward up to rounding: the weights enter as the exact
+   fp32 values scale * q + bias (scale and bias applied to each 32-weight dot
+   product) instead of being rounded to bf16 first, and fp32 sums run in
+   another order. Every weight of the k routed experts and of the
+   shared expert is read once, spread evenly over one workgroup per compute
+   unit as matrix-vector products: gate/up partial sums, h built by the last
+   workgroup to finish each 128-row slab, one device-wide barrier, then down
+   and the weighted combine. The launch relies on all of its workgroups
+   (at most one per compute unit) being resident together, as they are
+   when no other work holds the device's compute units.
    logits fp32 [T, E], x bf16 [T, H]; out bf16 [T, H]. Of the routing only
-   topk_ids, topk_w (written) and sched (sched[28..29] are the barrier's
-   counters, zero on entry and left zero; sched[30] is set to 1 if a barrier
-   wait gave up after about a second, which makes out invalid) are used.
-   Needs H a multiple of 512 (at most 8192), F a multiple of 128 (at most
-   4096). workspace: lily_moe_workspace_bytes(dims) bytes.
+   topk_ids, topk_w (written) and sched are used: sched[28..29] (barrier)
+   and sched[32 ..] (a counter per row and 128-row slab of F) are zero on
+   entry and left zero; sched[30] is set to 1 if the barrier wait gave up
+   after half a second, which makes out invalid.
+   Needs H a multiple of 512 (at most 4096), F a multiple of 256 with
+   (topk + 1) * F <= 16384 and T * (topk + 1) * F / 128 <= 512.
+   workspace: lily_moe_workspace_bytes(dims) bytes.
    Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (T > 4, sizes),
-   LILY_ERR_WORKSPACE, LILY_ERR_HIP (including a failed cooperative launch). */
+   LILY_ERR_WORKSPACE, LILY_ERR_HIP. */
 int lily_moe_decode(const lily_moe_dims* dims, const lily_moe_weights* weights,
                     const float* logits, const uint16_t* x, const lily_moe_routing* routing,
                     uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);

@@ -7,7 +7,8 @@
 // cost per token is the bytes moved). The grouped GEMM's tiles would put a
 // 32-row MFMA and a long K loop on a handful of workgroups; here the weights
 // are spread evenly over one workgroup per compute unit as matrix-vector
-// products on the VALU (bf16 dot2 instructions on the dequantised weights):
+// products on the VALU (bf16 dot2 instructions on the 4-bit values, scale
+// and bias applied to each 32-weight dot product):
 //   phase 0  top-k and softmax of every token (each workgroup, redundantly);
 //   phase A  gate/up: the packed blocks of all rows, in (row, gate/up, slab,
 //            group) order, cut into equal contiguous ranges, one per
@@ -38,8 +39,9 @@ constexpr int kDecBRounds = 6;       // phase B rounds per wavefront loaded at o
 constexpr int kDecPieces = 4;        // segments one phase A range may touch
 constexpr int kDecContrib = 8;       // phase A ranges one segment may span
 constexpr int kDecLdsWords = 8192;   // LDS: x rows (phase A) or h rows (phase B), bf16 pairs
-constexpr int kDecXWords = 16;       // x words staged per thread: 2 tokens of H <= 4096
-constexpr int kDecHWords = kDecLdsWords / kDecThreads;  // h words staged per thread
+constexpr int kDecXChunks = 4;       // x 16-byte chunks staged per thread: 2 tokens of H <= 4096
+constexpr int kDecHChunks = kDecLdsWords / 4 / kDecThreads;  // h chunks staged per thread
+constexpr int kDecSums = kDecLdsWords / 16;  // sums of 32 staged values
 constexpr int kDecPiece = 8;         // output rows per phase B unit
 constexpr long kSpinTicks = 50000000;  // device-wide barrier wait limit: 0.5 s at 100 MHz
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor: raw, 32-bit data format
@@ -56,10 +58,11 @@ struct DecodeArgs {
     const char* sh_down;
     int32_t* topk_ids;    // [T, k], written by workgroup 0
     float* topk_w;
-    float* pa;            // [grid][kDecPieces][128] phase A partial sums
+    float* pa;            // [segments][kDecContrib][128] phase A partial sums
     uint16_t* h;          // [R][F] bf16
     uint16_t* out;        // [T, H]
-    int32_t* ctr;         // [R][F / 128] arrivals per (row, slab): zero on entry, left zero
+    int32_t* ctr;         // arrivals per (row, slab), ctr_stride apart: zero on entry, left zero
+    int ctr_stride;       // ints between counters (up to a 128-byte line each)
     int32_t* bar;         // [2] barrier arrivals, exits: zero on entry, left zero
     int32_t* err;         // set to 1 if the barrier wait gave up
 };
@@ -89,23 +92,56 @@ __device__ __forceinline__ Slice load_slice(Rsrc r, int voff_q, int voff_s, int 
     return s;
 }
 
-// Dot product of a slice's 32 weights, rebuilt as bf16 exactly as in the
-// GEMMs, with 16 bf16 pairs of LDS (the matching k, in order).
-__device__ __forceinline__ float dot_slice(const Slice& s, const uint32_t* v) {
-    const float s512 = bf16_bits_to_float(s.sc) * 512.0f;
-    const float bias = bf16_bits_to_float(s.bi);
+// Vectors are staged in LDS as bf16 pairs permuted within each chunk of 8
+// elements: word j of chunk c holds elements (8c + j, 8c + j + 4). From
+// natural pairs p0..p3 of the chunk:
+__device__ __forceinline__ u32x4 permute_chunk(u32x4 p) {
+    u32x4 o;
+    o[0] = (p[0] & 0xFFFFu) | (p[2] << 16);
+    o[1] = (p[0] >> 16) | (p[2] & 0xFFFF0000u);
+    o[2] = (p[1] & 0xFFFFu) | (p[3] << 16);
+    o[3] = (p[1] >> 16) | (p[3] & 0xFFFF0000u);
+    return o;
+}
+
+// Dot product of a slice's 32 weights w = scale * q + bias with 32 staged
+// values v (16 permuted words) whose sum is vsum: scale * sum(q v) +
+// bias * vsum. The nibbles j and j + 4 of a weight word become the bf16 pair
+// (128 + q_j, 128 + q_j+4) with one byte permute each (exact: the exponent
+// byte 0x43 sets the scale to 1 on [128, 256)), so that
+// sum(q v) = sum((128 + q) v) - 128 vsum comes from bf16 dot2 instructions.
+// The weights enter exactly (fp32 scale and bias), not rounded to bf16 as in
+// the GEMMs.
+__device__ __forceinline__ float dot_slice(const Slice& s, const uint32_t* v, float vsum) {
     float acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        uint32_t wt[4];
-        dequant8(s.q[w], s512, bias, wt);
+        const uint32_t lo = s.q[w] & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
+        const uint32_t hi = (s.q[w] >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+        // bytes: 0-3 from the second operand, 4-7 from the first (0x43 each)
+        const uint32_t wt[4] = {__builtin_amdgcn_perm(0x43434343u, lo, 0x04020400u),   // 0, 4
+                                __builtin_amdgcn_perm(0x43434343u, hi, 0x04020400u),   // 1, 5
+                                __builtin_amdgcn_perm(0x43434343u, lo, 0x04030401u),   // 2, 6
+                                __builtin_amdgcn_perm(0x43434343u, hi, 0x04030401u)};  // 3, 7
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wt[e]),
                                                   __builtin_bit_cast(bf16x2, v[4 * w + e]), acc,
                                                   false);
     }
-    return acc;
+    const float scale = bf16_bits_to_float(s.sc), bias = bf16_bits_to_float(s.bi);
+    return fmaf(scale, acc, fmaf(-128.0f, scale, bias) * vsum);
+}
+
+// Sum of the 32 bf16 values in 16 LDS words (fp32).
+__device__ __forceinline__ float sum32(const uint32_t* v) {
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+        a += bf16_bits_to_float(v[n] & 0xFFFFu);
+        b += bf16_bits_to_float(v[n] >> 16);
+    }
+    return a + b;
 }
 
 // Workgroup barrier that waits for this thread's LDS accesses only: global
@@ -149,6 +185,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     __shared__ int32_t s_ids[kDecodeMaxT * kMaxTopk];
     __shared__ float s_w[kDecodeMaxT * kMaxTopk];
     __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDecLdsWords];
+    __shared__ float s_vsum[kDecSums];  // sums of 32 consecutive staged values
     __shared__ float s_red[kDecPieces][kPackRows];
     __shared__ float s_bred[kDecThreads / kWave][kDecPiece];
     __shared__ int s_last[kDecPieces];
@@ -176,17 +213,21 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     const int i = tid % kPackRows, hh = tid / kPackRows;
     const int x_words = (t_lo + 1 < a.T ? 2 : 1) * (H / 2);
     const Rsrc x_rs = make_rsrc(a.x + (size_t)t_lo * H, x_words * 4);
-    uint32_t xr[kDecXWords];
+    u32x4 xr[kDecXChunks];
 #pragma unroll
-    for (int n = 0; n < kDecXWords; ++n)  // x_words is a multiple of 256
-        if (n * kDecThreads < x_words)
-            xr[n] = __builtin_amdgcn_raw_buffer_load_b32(x_rs, tid * 4, n * kDecThreads * 4, 0);
+    for (int n = 0; n < kDecXChunks; ++n)  // chunks past the end read 0
+        if (n * kDecThreads * 4 < x_words)
+            xr[n] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, (tid + n * kDecThreads) * 16, 0, 0);
 
     // Phase 0: every workgroup routes every token (wave t takes token t).
     if (wave < a.T) topk_one_token(a.logits, wave, a.E, k, s_ids, s_w);
 #pragma unroll
-    for (int n = 0; n < kDecXWords; ++n)
-        if (n * kDecThreads < x_words) s_buf[tid + n * kDecThreads] = xr[n];
+    for (int n = 0; n < kDecXChunks; ++n) {
+        const int c = tid + n * kDecThreads;
+        if (c * 4 < x_words) *reinterpret_cast<u32x4*>(s_buf + 4 * c) = permute_chunk(xr[n]);
+    }
+    __syncthreads();
+    if (tid < x_words / 16) s_vsum[tid] = sum32(s_buf + 16 * tid);
     __syncthreads();
     if (wg == 0 && tid < a.T * k) {
         a.topk_ids[tid] = s_ids[tid];
@@ -270,7 +311,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int n = 0; n < kDecBatch; ++n) {
             if (n < nb) {
-                const float d = dot_slice(sl[n], s_buf + xoff[n]);
+                const float d = dot_slice(sl[n], s_buf + xoff[n], s_vsum[xoff[n] / 16]);
 #pragma unroll
                 for (int p = 0; p < kDecPieces; ++p)
                     if (p == piece[n]) accp[p] += d;
@@ -286,73 +327,76 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         for (int p = 0; p < kDecPieces; ++p) s_red[p][i] = accp[p];
     }
     __syncthreads();
+    // slot of this range among the contributors of segment seg0 + p: the
+    // first piece may continue a segment that earlier ranges started
+    const int c0 = wg - range_owner(seg0 * nkg, NB, G);
     if (hh == 0) {
 #pragma unroll
         for (int p = 0; p < kDecPieces; ++p)
             if (p < npieces)
-                __hip_atomic_store(a.pa + ((size_t)wg * kDecPieces + p) * kPackRows + i,
-                                   accp[p] + s_red[p][i], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(
+                    a.pa + ((size_t)(seg0 + p) * kDecContrib + (p == 0 ? c0 : 0)) * kPackRows + i,
+                    accp[p] + s_red[p][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // Count this range's segments in; the last contribution to a (row, slab)
-    // (of its gate and up segments) builds that slab of h.
-    if (tid == 0) {
-        for (int p = 0; p < npieces; ++p) {
-            const int sg = seg0 + p;
-            const int r = sg / (2 * nsf), s = sg % nsf;
-            int total = 0;
-            for (int m = 0; m < 2; ++m) {
-                const int msg = (r * 2 + m) * nsf + s;
-                total += range_owner(msg * nkg + nkg - 1, NB, G) - range_owner(msg * nkg, NB, G) + 1;
-            }
-            int32_t* c = a.ctr + r * nsf + s;
-            const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last[p] = (prev == total - 1);
-            if (prev == total - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    __syncthreads();
-    for (int p = 0; p < npieces; ++p) {
-        if (!s_last[p] || tid >= kPackRows / 2) continue;
-        const int sg = seg0 + p;
+    // Count this range's segments in (thread p counts piece p); the last
+    // contribution to a (row, slab) (of its gate and up segments) builds that
+    // slab of h.
+    if (tid < npieces) {
+        const int sg = seg0 + tid;
         const int r = sg / (2 * nsf), s = sg % nsf;
-        // every partial of both rows of this thread, gate and up, loaded at once
-        float v[2][2][kDecContrib];
-        int nw[2];
-#pragma unroll
+        int total = 0;
         for (int m = 0; m < 2; ++m) {
             const int msg = (r * 2 + m) * nsf + s;
-            const int w_first = range_owner(msg * nkg, NB, G);
-            nw[m] = range_owner(msg * nkg + nkg - 1, NB, G) - w_first + 1;
-#pragma unroll
-            for (int c = 0; c < kDecContrib; ++c) {
-                const int w = w_first + min(c, nw[m] - 1);
-                const int piece = msg - range_begin(w, NB, G) / nkg;
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    v[q][m][c] = __hip_atomic_load(
-                        a.pa + ((size_t)w * kDecPieces + piece) * kPackRows + 2 * tid + q,
-                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            total += range_owner(msg * nkg + nkg - 1, NB, G) - range_owner(msg * nkg, NB, G) + 1;
         }
-        float hv[2];
+        int32_t* c = a.ctr + (r * nsf + s) * a.ctr_stride;
+        const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last[tid] = (prev == total - 1);
+        if (prev == total - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    // thread (m, row): the partials of row `row` of the gate (m = 0) or up
+    // segment of each slab this workgroup builds, all loaded before any h
+    // store, added in workgroup order
+    const int m = tid / kPackRows, row = tid % kPackRows;
+    float sums[kDecPieces];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            float sum[2];
+    for (int p = 0; p < kDecPieces; ++p) {
+        sums[p] = 0.0f;
+        if (p < npieces && s_last[p]) {  // the same in every thread
+            const int sg = seg0 + p;
+            const int r = sg / (2 * nsf), s = sg % nsf;
+            const int msg = (r * 2 + m) * nsf + s;
+            const int nw = range_owner(msg * nkg + nkg - 1, NB, G) - range_owner(msg * nkg, NB, G) + 1;
+            const float* src = a.pa + (size_t)msg * kDecContrib * kPackRows + row;
+            float v[kDecContrib];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                float acc = 0.0f;
+            for (int c = 0; c < kDecContrib; ++c)
+                v[c] = __hip_atomic_load(src + min(c, nw - 1) * kPackRows, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                for (int c = 0; c < kDecContrib; ++c)
-                    if (c < nw[m]) acc += v[q][m][c];
-                sum[m] = acc;
-            }
-            hv[q] = silu(sum[0]) * sum[1];
+            for (int c = 0; c < kDecContrib; ++c)
+                if (c < nw) sums[p] += v[c];
         }
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h + (size_t)r * F + s * kPackRows) + tid,
-                           pack_bf16x2(hv[0], hv[1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int p = 0; p < kDecPieces; ++p) {
+        if (p < npieces && s_last[p]) {
+            const int sg = seg0 + p;
+            const int r = sg / (2 * nsf), s = sg % nsf;
+            s_red[m][row] = sums[p];
+            __syncthreads();
+            if (tid < kPackRows / 2) {
+                const float h0 = silu(s_red[0][2 * tid]) * s_red[1][2 * tid];
+                const float h1 = silu(s_red[0][2 * tid + 1]) * s_red[1][2 * tid + 1];
+                __hip_atomic_store(
+                    reinterpret_cast<uint32_t*>(a.h + (size_t)r * F + s * kPackRows) + tid,
+                    pack_bf16x2(h0, h1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+        }
     }
     device_barrier(a.bar, G, a.err);
 
@@ -365,14 +409,24 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         if (t != t_staged) {
             __syncthreads();  // earlier readers of s_buf are done
             const uint32_t* hg = reinterpret_cast<const uint32_t*>(a.h + (size_t)t * (k + 1) * F);
-            uint32_t hr[kDecHWords];
+            u32x4 hr[kDecHChunks];
 #pragma unroll
-            for (int n = 0; n < kDecHWords; ++n)
-                hr[n] = __hip_atomic_load(hg + min(tid + n * kDecThreads, h_words - 1),
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int n = 0; n < kDecHChunks; ++n) {
+                if (n * kDecThreads < h_words / 4) {
+                    const int c = min(tid + n * kDecThreads, h_words / 4 - 1);
 #pragma unroll
-            for (int n = 0; n < kDecHWords; ++n)
-                if (tid + n * kDecThreads < h_words) s_buf[tid + n * kDecThreads] = hr[n];
+                    for (int e = 0; e < 4; ++e)
+                        hr[n][e] = __hip_atomic_load(hg + 4 * c + e, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < kDecHChunks; ++n) {
+                const int c = tid + n * kDecThreads;
+                if (c < h_words / 4) *reinterpret_cast<u32x4*>(s_buf + 4 * c) = permute_chunk(hr[n]);
+            }
+            __syncthreads();
+            for (int q = tid; q < h_words / 16; q += kDecThreads) s_vsum[q] = sum32(s_buf + 16 * q);
             __syncthreads();
             t_staged = t;
         }
@@ -385,7 +439,8 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
             }
 #pragma unroll
             for (int n = 0; n < kDecBRounds; ++n)
-                if (wv + 4 * (n0 + n) < NRB) acc = fmaf(pw[n], dot_slice(pb[n], s_buf + ph[n]), acc);
+                if (wv + 4 * (n0 + n) < NRB)
+                    acc = fmaf(pw[n], dot_slice(pb[n], s_buf + ph[n], s_vsum[ph[n] / 16]), acc);
         }
         // the next unit's first rounds, in flight during this unit's sums
         if (u + 1 < ub1) {
@@ -446,17 +501,17 @@ static int decode_grid(const lily_moe_dims& d) {
 size_t decode_workspace_bytes(const lily_moe_dims& d) {
     if (d.T > kDecodeMaxT) return 0;
     const size_t R = (size_t)d.T * (d.topk + 1);
-    return (size_t)kDecMaxGrid * kDecPieces * kPackRows * sizeof(float) +
-           R * d.F * sizeof(uint16_t);
+    const size_t segments = R * 2 * (d.F / kPackRows);
+    return segments * kDecContrib * kPackRows * sizeof(float) + R * d.F * sizeof(uint16_t);
 }
 
 int decode_supported(const lily_moe_dims& d) {
     if (d.T > kDecodeMaxT)
         return set_error(LILY_ERR_UNSUPPORTED, "T = %d; lily_moe_decode serves T <= %d", d.T,
                          kDecodeMaxT);
-    if (d.H % (2 * kDecThreads) || d.H > kDecXWords * kDecThreads)
+    if (d.H % (2 * kDecThreads) || d.H > kDecXChunks * 4 * kDecThreads)
         return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 512, at most %d",
-                         d.H, kDecXWords * kDecThreads);
+                         d.H, kDecXChunks * 4 * kDecThreads);
     if (d.F % (4 * kGroup) || (long)(d.topk + 1) * d.F > 2L * kDecLdsWords)
         return set_error(LILY_ERR_UNSUPPORTED,
                          "F = %d must be a multiple of 256 with (topk + 1) * F <= %d", d.F,
@@ -490,9 +545,16 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
     a.topk_ids = r.topk_ids;
     a.topk_w = r.topk_w;
     a.pa = static_cast<float*>(workspace);
-    a.h = reinterpret_cast<uint16_t*>(a.pa + (size_t)kDecMaxGrid * kDecPieces * kPackRows);
+    const size_t segments = (size_t)d.T * (d.topk + 1) * 2 * (d.F / kPackRows);
+    a.h = reinterpret_cast<uint16_t*>(a.pa + segments * kDecContrib * kPackRows);
     a.out = out;
+    // Counters on lines of their own where the sched array has room: device
+    // scope atomics on one line are serialised.
     a.ctr = r.sched + kQueueInts;
+    const long n_ctr = (long)d.T * (d.topk + 1) * (d.F / kPackRows);
+    a.ctr_stride = 1;
+    while (a.ctr_stride < 32 && 2 * a.ctr_stride * n_ctr <= kSchedInts - kQueueInts)
+        a.ctr_stride *= 2;
     a.bar = r.sched + kDecodeBarrier;
     a.err = r.sched + kDecodeBarrier + 2;
     // A phase A range touches at most kDecPieces segments and two tokens; a

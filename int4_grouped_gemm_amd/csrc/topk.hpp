@@ -41,44 +41,39 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(max(a, b), max(c, d));
 }
 
-// Top-k and softmax of one token by one wavefront. Lane l holds the logits
-// of experts l, l + 64, ... as order-preserving keys; a taken expert's key
-// becomes 0, below every real key. Each round takes the wavefront maximum
-// and, among the experts holding it, the lowest index (ballots in expert
-// order).
-__device__ __forceinline__ void topk_one_token(const float* __restrict__ logits, int t, int E,
-                                               int k, int32_t* __restrict__ topk_ids,
-                                               float* __restrict__ topk_w) {
+// Top-k and softmax of one token by one wavefront, NPER = ceil(E / 64)
+// logits per lane. Lane l holds the logits of experts l, l + 64, ... as
+// order-preserving keys; a taken expert's key becomes 0, below every real
+// key. Each round takes the wavefront maximum and, among the experts holding
+// it, the lowest index (ballots in expert order).
+template <int NPER>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
+                                           int32_t* __restrict__ topk_ids,
+                                           float* __restrict__ topk_w) {
     const int lane = threadIdx.x % kWave;
     const float* row = logits + (size_t)t * E;
-    const int nper = (E + kWave - 1) / kWave;
     // Every lane issues all its loads before the first use (indexes clamped
     // into the row, so none is conditional); a load per branch would wait
     // for each one in turn.
-    float lv[kMaxPerLane];
+    float lv[NPER];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < NPER; ++i) {
         const int e = lane + i * kWave;
         lv[i] = row[e < E ? e : E - 1];
     }
-    uint32_t key[kMaxPerLane];
+    uint32_t key[NPER];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + i * kWave;
-        key[i] = (i < nper && e < E) ? ordered_bits(lv[i]) : 0u;
-    }
+    for (int i = 0; i < NPER; ++i) key[i] = (lane + i * kWave < E) ? ordered_bits(lv[i]) : 0u;
     int my_id = 0;
     float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
-        uint32_t best = 0;
+        uint32_t best = key[0];
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (i < nper) best = max(best, key[i]);
+        for (int i = 1; i < NPER; ++i) best = max(best, key[i]);
         best = wave_max_u32(best);
         int e_sel = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            if (i >= nper) break;
+        for (int i = 0; i < NPER; ++i) {
             const uint64_t hit = __ballot(key[i] == best);
             if (hit) {
                 e_sel = i * kWave + (int)__ffsll((long long)hit) - 1;
@@ -87,7 +82,7 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ logits,
         }
         if (lane == e_sel % kWave) {
 #pragma unroll
-            for (int i = 0; i < kMaxPerLane; ++i)
+            for (int i = 0; i < NPER; ++i)
                 if (i == e_sel / kWave) key[i] = 0u;
         }
         if (lane == j) {
@@ -103,6 +98,22 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ logits,
     if (lane < k) {
         topk_ids[(size_t)t * k + lane] = my_id;
         topk_w[(size_t)t * k + lane] = ex / sum;
+    }
+}
+
+// Top-k and softmax of token t (E <= kMaxExperts) by one wavefront.
+__device__ __forceinline__ void topk_one_token(const float* __restrict__ logits, int t, int E,
+                                               int k, int32_t* __restrict__ topk_ids,
+                                               float* __restrict__ topk_w) {
+    switch ((E + kWave - 1) / kWave) {
+        case 1: topk_token<1>(logits, t, E, k, topk_ids, topk_w); break;
+        case 2: topk_token<2>(logits, t, E, k, topk_ids, topk_w); break;
+        case 3: topk_token<3>(logits, t, E, k, topk_ids, topk_w); break;
+        case 4: topk_token<4>(logits, t, E, k, topk_ids, topk_w); break;
+        case 5: topk_token<5>(logits, t, E, k, topk_ids, topk_w); break;
+        case 6: topk_token<6>(logits, t, E, k, topk_ids, topk_w); break;
+        case 7: topk_token<7>(logits, t, E, k, topk_ids, topk_w); break;
+        default: topk_token<kMaxPerLane>(logits, t, E, k, topk_ids, topk_w); break;
     }
 }
 

@@ -224,7 +224,7 @@ def test_forward_small_T_split_k(T, tile_m):
 @pytest.mark.parametrize("name,T", [("decode40", 1), ("prefill512", 2), ("prefill512", 4),
                                     ("prefill2048_zipf", 3)])
 def test_decode_fused(name, T):
-    """lily_moe_decode (route and forward in one cooperative launch) against
+    """lily_moe_decode (route and forward in one launch) against
     the oracle: top-k ids exact, weights within 2e-6, outputs within the
     tolerance; run twice bit-identically; barrier counters left zero."""
     cfg = S.CONFIGS[name]
