@@ -34,7 +34,7 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill2048_zipf.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "int4_grouped_gemm_amd", "csrc", f)
-                  for f in ("gemm_w4.hip", "route.hip", "common.hpp")]
+                  for f in ("gemm_w4.hip", "route.hip", "common.hpp", "topk.hpp", "w4.hpp")]
 
 
 def kernel_source_hash() -> str:
