@@ -78,6 +78,8 @@ CONFIGS: Dict[str, LayerConfig] = {
         LayerConfig("stack40_T8192", 3, T=2048, H=2048, F=512, E=256, k=8, layers=40,
                     total_tokens=8192),
         LayerConfig("decode40", 4, T=1, H=2048, F=512, E=256, k=8, layers=40, steps=256),
+        # one layer call at the long-prompt size, uniform routing (tile-height sweep)
+        LayerConfig("prefill8192", 5, T=8192, H=2048, F=512, E=256, k=8),
     )
 }
 
