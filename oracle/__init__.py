@@ -54,6 +54,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.oracle_residual_norm.restype = ctypes.c_int
     lib.oracle_residual_norm.argtypes = [ctypes.c_int, ctypes.c_int, _c_f32p, _c_u16p, _c_u16p,
                                          ctypes.c_float]
+    lib.oracle_router.restype = ctypes.c_int
+    lib.oracle_router.argtypes = [ctypes.c_int] * 3 + [_c_u16p, _c_u16p, _c_f32p, _c_f32p]
     lib.oracle_float_to_bf16.restype = ctypes.c_uint16
     lib.oracle_float_to_bf16.argtypes = [ctypes.c_float]
     lib.oracle_threads.restype = ctypes.c_int
@@ -96,6 +98,24 @@ def route(logits: np.ndarray, k: int, tile_m: int, lib: Optional[ctypes.CDLL] = 
     out["block_expert"] = out["block_expert"][:nb].copy()
     out["block_row0"] = out["block_row0"][:nb].copy()
     return out
+
+
+def router(x: np.ndarray, w: np.ndarray, lib: Optional[ctypes.CDLL] = None):
+    """Router projection of bf16 x [T, H] by bf16 Wr [E, H]: (logits, absdot),
+    float32 [T, E] each; absdot = sum |x w| bounds fp32 summation error."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    T, H = x.shape
+    E = w.shape[0]
+    assert w.shape[1] == H
+    logits = np.zeros((T, E), np.float32)
+    absdot = np.zeros((T, E), np.float32)
+    rc = lib.oracle_router(T, H, E, _p(x, _c_u16p), _p(w, _c_u16p), _p(logits, _c_f32p),
+                           _p(absdot, _c_f32p))
+    if rc != 0:
+        raise OracleError(f"oracle_router failed: {rc}")
+    return logits, absdot
 
 
 def max_blocks_for(T: int, E: int, k: int, tile_m: int) -> int:

@@ -17,6 +17,8 @@
  *    products accumulate in FP32 (same section).
  *  - The router scores E experts and picks k of them; a shared expert also
  *    processes every token (ainew, section on the three workload shapes).
+ *    Where the scores come from x, they are the router projection x.Wr^T
+ *    (bf16 inputs, summed in double here).
  *  - Per MoE layer the route is: a per-expert histogram, a prefix scan, a
  *    scatter of tokens into expert order and a block map for the grouped
  *    GEMM (ainew, section "Prefill").
@@ -365,6 +367,31 @@ int oracle_residual_norm(int T, int H, float* r, const uint16_t* out_bf16, uint1
 }
 
 /* Expose the oracle's own rounding for the pins. */
+/* Router projection (the router scores every expert for each token: ainew,
+   section on the three workload shapes): logits[t, e] = sum_h x[t, h] *
+   w[e, h] with bf16 inputs, summed in double and rounded once to float.
+   absdot[t, e] = sum_h |x[t, h] * w[e, h]| (double, then float) bounds the
+   error of any fp32 summation order; either output may be NULL. */
+int oracle_router(int T, int H, int E, const uint16_t* x, const uint16_t* w, float* logits,
+                  float* absdot) {
+    if (T < 1 || H < 1 || E < 1 || !x || !w) return -1;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0, mag = 0.0;
+            for (int h = 0; h < H; ++h) {
+                const double p = (double)bf16_to_float(x[(size_t)t * H + h]) *
+                                 (double)bf16_to_float(w[(size_t)e * H + h]);
+                acc += p;
+                mag += fabs(p);
+            }
+            if (logits) logits[(size_t)t * E + e] = (float)acc;
+            if (absdot) absdot[(size_t)t * E + e] = (float)mag;
+        }
+    }
+    return 0;
+}
+
 uint16_t oracle_float_to_bf16(float f) { return float_to_bf16(f); }
 int oracle_threads(void) {
 #ifdef _OPENMP

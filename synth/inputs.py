@@ -37,6 +37,7 @@ GROUP = 64
 X_KEY = 1_000_000
 LOGIT_KEY = 2_000_000
 ZIPF_KEY = 3_000_000
+ROUTER_KEY = 4_000_000
 ZIPF_S = 1.1
 
 GATE, UP, DOWN = 0, 1, 2
@@ -190,6 +191,14 @@ def router_logits(cfg: LayerConfig, layer: int = 0, index: int = 0, seed: int = 
     if cfg.zipf:
         lg = lg + zipf_log_bias(cfg, seed)[None, :]
     return np.ascontiguousarray(lg, dtype=np.float32)
+
+
+def router_weights(cfg: LayerConfig, layer: int = 0, seed: int = 0) -> np.ndarray:
+    """Router projection W_r, bf16 bits [E, H], drawn N(0, 1/H) so that
+    x W_r^T of N(0,1) activations has unit variance, like the logits above."""
+    g = rng(seed, cfg.cfg_id, layer, ROUTER_KEY, 0)
+    w = g.standard_normal((cfg.E, cfg.H), dtype=np.float32) * np.float32(1.0 / np.sqrt(cfg.H))
+    return f32_to_bf16_bits(w)
 
 
 def iter_layer_weights(cfg: LayerConfig, seed: int = 0) -> Iterator[LayerWeights]:

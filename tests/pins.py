@@ -365,6 +365,30 @@ def pin_forward_special_cases(lib):
     assert norm_err(acc, ref) <= 1e-5, "single-token GEMV"
 
 
+def pin_router(lib):
+    """Router projection against a float64 numpy matmul of the widened bf16
+    inputs (a different summation, so at most 1 ulp of the final fp32
+    rounding apart), on non-square shapes so a transposed index shows; a
+    one-hot x picks a column of Wr exactly."""
+    rng = np.random.default_rng(7)
+    T, H, E = 5, 192, 7
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = S.f32_to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.1))
+    lg, ad = oracle.router(x, w, lib=lib)
+    xf = S.bf16_bits_to_f32(x).astype(np.float64)
+    wf = S.bf16_bits_to_f32(w).astype(np.float64)
+    ref = (xf @ wf.T).astype(np.float32)
+    assert np.all(np.abs(lg - ref) <= np.spacing(np.abs(ref))), "router logits"
+    mag = (np.abs(xf) @ np.abs(wf).T).astype(np.float32)
+    assert np.all(np.abs(ad - mag) <= np.spacing(mag)), "router |x w| sums"
+    # one-hot rows: token t selects column h_t of every router row
+    cols = np.array([0, 3, 64, 130, 191])
+    onehot = np.zeros((T, H), np.uint16)
+    onehot[np.arange(T), cols] = S.f32_to_bf16_bits(np.ones(T, np.float32))
+    lg1, _ = oracle.router(onehot, w, lib=lib)
+    assert np.array_equal(lg1, wf[:, cols].T.astype(np.float32)), "one-hot router row"
+
+
 def pin_residual_norm(lib):
     g = np.random.default_rng(3)
     T, H = 4, 256
@@ -383,4 +407,4 @@ def pin_residual_norm(lib):
 
 ALL_PINS = [pin_dequant_closed_form, pin_dequant_golden, pin_nibble_order, pin_group_axis,
             pin_route_brute_force, pin_route_ties, pin_route_golden, pin_forward_dense,
-            pin_forward_h_rounding, pin_forward_special_cases, pin_residual_norm]
+            pin_forward_h_rounding, pin_forward_special_cases, pin_router, pin_residual_norm]

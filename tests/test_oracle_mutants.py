@@ -46,6 +46,11 @@ MUTANTS = {
                             "float w = topk_w[(size_t)t * k];"),
     "final_not_rounded_rne": ("out_bf16[(size_t)i * H + n] = float_to_bf16(acc[n]);",
                               "out_bf16[(size_t)i * H + n] = (uint16_t)(((union {float f; uint32_t u;}){acc[n]}).u >> 16);"),
+    "router_weight_transposed": ("(double)bf16_to_float(w[(size_t)e * H + h]);",
+                                 "(double)bf16_to_float(w[(size_t)h * E + e]);"),
+    "router_abs_signed": ("mag += fabs(p);", "mag += p;"),
+    "router_float_sum": ("            double acc = 0.0, mag = 0.0;",
+                         "            float acc = 0.0f; double mag = 0.0;"),
     "rmsnorm_mean": ("float inv = 1.0f / sqrtf(ss / (float)H + eps);",
                      "float inv = 1.0f / sqrtf(ss + eps);"),
 }
