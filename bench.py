@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--tile-m", type=int, default=128)
     ap.add_argument("--decode-path", default="fused", choices=["fused", "layer"],
                     help="decode40: lily_moe_decode (one launch per layer) or route + forward")
+    ap.add_argument("--router", action="store_true",
+                    help="start each step from x: the router projection x.Wr^T (lily_moe_router) "
+                         "computes the logits inside the timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of layer 0 the CPU oracle computes for the baseline")
@@ -70,6 +73,7 @@ def stage_work(cfg, P):
     for the memory-bound stages)."""
     rows = P + cfg.T
     return {
+        "router": ("mfma", 2.0 * cfg.T * cfg.H * cfg.E),
         "route": ("hbm", cfg.T * cfg.E * 4 + P * 4 * 4 + cfg.T * cfg.k * 4),
         "gate_up": ("mfma", 2.0 * rows * cfg.H * 2 * cfg.F),
         "down": ("mfma", 2.0 * rows * cfg.F * cfg.H),
@@ -101,10 +105,14 @@ def main():
 
     # ---- inputs, resident in HBM before timing
     t_gen = time.time()
-    weights, logits = [], []
+    weights, logits, routers = [], [], []
     for layer in range(args.layers):
         weights.append(L.weights_from_host(S.layer_weights(cfg, layer), dev))
-        logits.append(torch.from_numpy(S.router_logits(cfg, layer)).to(dev))
+        if args.router:
+            routers.append(torch.from_numpy(S.router_weights(cfg, layer).view(np.int16)).to(dev))
+            logits.append(torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev))
+        else:
+            logits.append(torch.from_numpy(S.router_logits(cfg, layer)).to(dev))
     x = torch.from_numpy(S.activations(cfg).view(np.int16)).to(dev)
     routing = L.alloc_routing(d, dev)
     ws = L.alloc_workspace(d, dev)
@@ -113,29 +121,29 @@ def main():
     print(f"# inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    stages = ("route", "gate_up", "down", "combine")
+    stages = (("router",) if args.router else ()) + ("route", "gate_up", "down", "combine")
 
     def step(i, ev=None):
         layer = i % args.layers
         w = weights[layer]
+        calls = []
+        if args.router:
+            calls.append(lambda: L.lily_moe_router(d, routers[layer], x, logits[layer], stream))
+        calls += [lambda: L.lily_moe_route(d, logits[layer], routing, stream),
+                  lambda: L.lily_moe_gate_up(d, w, x, routing, ws, stream),
+                  lambda: L.lily_moe_down(d, w, routing, ws, stream),
+                  lambda: L.lily_moe_combine(d, routing, ws, out, stream)]
+        for j, call in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            call()
         if ev is not None:
-            ev[0].record(stream)
-        L.lily_moe_route(d, logits[layer], routing, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        L.lily_moe_gate_up(d, w, x, routing, ws, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        L.lily_moe_down(d, w, routing, ws, stream)
-        if ev is not None:
-            ev[3].record(stream)
-        L.lily_moe_combine(d, routing, ws, out, stream)
-        if ev is not None:
-            ev[4].record(stream)
+            ev[len(calls)].record(stream)
 
     for i in range(args.warmup):
         step(i)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -169,7 +177,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         tr = json.loads([ln for ln in open(TRAFFIC_FILE) if ln.startswith("{")][0])
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("stage") == dom \
-                and tr.get("tile_m") == args.tile_m:
+                and tr.get("tile_m") == args.tile_m and tr.get("workload") == args.workload \
+                and not args.router:
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom}
@@ -200,6 +209,8 @@ def main():
             "topk": cfg.k,
             "shared_experts": 1, "group": 64, "tile_m": args.tile_m,
             "layer_weight_sets": args.layers,
+            "logits": "router projection x.Wr^T in the step" if args.router
+                      else "given (router_logits)",
             "routing": "logits N(0,1) + per-expert Zipf(1.1) log-bias" if cfg.zipf
                        else "logits N(0,1)",
             "weights": "int4 q~U{0..15}, bf16 scale~U(0.005,0.02), bf16 bias~N(0,0.01)",

@@ -170,6 +170,18 @@ size_t lily_w4_packed_bytes(int32_t n, int32_t N, int32_t K, int32_t group);
 int lily_w4_pack(const lily_w4* w, int32_t n, int32_t N, int32_t K, int32_t group, void* packed,
                  void* stream);
 
+/* Router projection, the step before lily_moe_route when a layer starts
+   from its activations: logits[t, e] = sum_h x[t, h] * w_router[e, h]
+   (the router scores every expert for each token: Lily articles, section on
+   the three workload shapes). x bf16 [T, H], w_router bf16 [E, H] (row e
+   scores expert e), logits fp32 [T, E], all row-major device memory. The
+   bf16 products are exact in fp32 and summed in fp32 (in another order than
+   a sequential loop). Only T, H, E of dims are used beyond the common
+   checks; H must be a multiple of 256. Errors: LILY_ERR_INVALID_ARG (null
+   or misaligned pointer, bad dims), LILY_ERR_UNSUPPORTED (H), LILY_ERR_HIP. */
+int lily_moe_router(const lily_moe_dims* dims, const uint16_t* w_router, const uint16_t* x,
+                    float* logits, void* stream);
+
 /* Routing of one MoE layer: top-k and softmax per token, histogram,
    exclusive scan, stable scatter and block map, all enqueued on `stream`
    with no host synchronisation.

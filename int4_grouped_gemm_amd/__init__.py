@@ -24,7 +24,7 @@ LILY_ERR_WORKSPACE = -3
 LILY_ERR_HIP = -4
 
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
-           "lily_w4_pack", "lily_moe_route", "lily_moe_forward", "lily_moe_gate_up",
+           "lily_w4_pack", "lily_moe_router", "lily_moe_route", "lily_moe_forward", "lily_moe_gate_up",
            "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_residual_norm",
            "lily_last_error")
 LILY_SCHED_INTS = 1056
@@ -83,6 +83,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_w4_pack.restype = ctypes.c_int
     lib.lily_w4_pack.argtypes = [P(LilyW4), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_moe_router.restype = ctypes.c_int
+    lib.lily_moe_router.argtypes = [P(LilyMoeDims), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
     lib.lily_moe_route.restype = ctypes.c_int
     lib.lily_moe_route.argtypes = [P(LilyMoeDims), ctypes.c_void_p, P(LilyMoeRouting),
                                    ctypes.c_void_p]
@@ -220,6 +223,14 @@ def lily_w4_packed_bytes(n: int, N: int, K: int, group: int = 64) -> int:
 def lily_w4_pack(w: W4, n: int, N: int, K: int, packed, group: int = 64, stream=None) -> None:
     lib = load()
     rc = lib.lily_w4_pack(ctypes.byref(w.c()), n, N, K, group, _ptr(packed), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_router(d: LilyMoeDims, w_router, x, logits, stream=None) -> None:
+    """logits fp32 [T, E] = x [T, H] (bf16 bits) times w_router [E, H] (bf16 bits)^T."""
+    lib = load()
+    rc = lib.lily_moe_router(ctypes.byref(d), _ptr(w_router), _ptr(x), _ptr(logits),
+                             _stream(stream))
     _check(rc, lib)
 
 

@@ -42,6 +42,8 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
                   hipStream_t stream);
 int launch_residual_norm(int T, int H, float* r, const uint16_t* out, uint16_t* x_next,
                          float eps, hipStream_t stream);
+int launch_router(const lily_moe_dims& d, const uint16_t* w_router, const uint16_t* x,
+                  float* logits, hipStream_t stream);
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -179,6 +181,18 @@ int lily_w4_pack(const lily_w4* w, int32_t n, int32_t N, int32_t K, int32_t grou
     REQUIRE_PTR(w->bias);
     REQUIRE_PTR(packed);
     return launch_pack(*w, n, N, K, packed, reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_router(const lily_moe_dims* dims, const uint16_t* w_router, const uint16_t* x,
+                    float* logits, void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->H % 256)
+        return set_error(LILY_ERR_UNSUPPORTED, "router: H = %d is not a multiple of 256", dims->H);
+    REQUIRE_PTR(w_router);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(logits);
+    return launch_router(*dims, w_router, x, logits, reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_moe_route(const lily_moe_dims* dims, const float* logits,

@@ -256,3 +256,41 @@ def test_decode_fused(name, T):
     torch.cuda.synchronize()
     assert torch.equal(again, out), "fused decode is not deterministic"
     assert not np.any(r.sched.cpu().numpy()), "barrier counters and error flag must be zero"
+
+
+# ------------------------------------------------------------------- router
+
+@pytest.mark.parametrize("name,T", [("tiny", 32), ("tiny", 7), ("prefill512", 512),
+                                    ("prefill512", 77), ("decode40", 1),
+                                    ("prefill2048_zipf", 2048)])
+def test_router_projection(name, T):
+    """lily_moe_router against the oracle: every logit within the fp32
+    summation bound 2 H 2^-24 sum|x w| of the double-precision reference; the
+    route of the GPU logits bit-exact with the oracle's route of the same
+    logits; and every expert the GPU logits select is a valid choice under the
+    reference logits (no unselected expert beats it by more than the bound)."""
+    cfg = S.CONFIGS[name]
+    _flush(f"router {name} T={T}")
+    x = S.activations(cfg, 0, T=T)
+    w = S.router_weights(cfg)
+    ref, absdot = oracle.router(x, w)
+    d = L.dims(T, cfg.H, cfg.F, cfg.E, cfg.k, 32)
+    lg = torch.full((T, cfg.E), float("nan"), dtype=torch.float32, device="cuda")
+    L.lily_moe_router(d, G.to_dev_bits(w), G.to_dev_bits(x), lg)
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy()
+    bound = 2.0 * cfg.H * 2.0 ** -24 * absdot.astype(np.float64) + 1e-30
+    err = np.abs(got.astype(np.float64) - ref)
+    _flush(f"  max error / bound {np.max(err / bound):.3f}")
+    assert np.all(err <= bound), "router logits outside the fp32 summation bound"
+    # the route of the GPU logits
+    gpu_r = G.routing_to_host(G.route_gpu(d, got))
+    G.compare_routing(gpu_r, oracle.route(got, cfg.k, 32), 32)
+    # validity of the selection under the reference logits
+    sel = gpu_r["topk_ids"].astype(np.int64)
+    chosen = np.take_along_axis(ref, sel, axis=1)
+    mask = np.ones_like(ref, dtype=bool)
+    np.put_along_axis(mask, sel, False, axis=1)
+    best_other = np.where(mask, ref, -np.inf).max(axis=1)
+    slack = 2.0 * bound.max(axis=1)
+    assert np.all(chosen.min(axis=1) >= best_other - slack), "a selected expert is not in the top-k"
