@@ -234,19 +234,19 @@ int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
    fp32 values scale * q + bias (scale and bias applied to each 32-weight dot
    product) instead of being rounded to bf16 first, and fp32 sums run in
    another order. Every weight of the k routed experts and of the
-   shared expert is read once, spread evenly over one workgroup per compute
-   unit as matrix-vector products: gate/up partial sums, h built by the last
-   workgroup to finish each 128-row slab, one device-wide barrier, then down
-   and the weighted combine. The launch relies on all of its workgroups
-   (at most one per compute unit) being resident together, as they are
-   when no other work holds the device's compute units.
+   shared expert is read once, spread over one workgroup per compute unit
+   as matrix-vector products: gate/up by one wavefront per (row, 8 features)
+   over all of K, which forms that part of h itself; one device-wide
+   barrier; then down and the weighted combine. The launch relies on all of
+   its workgroups (at most one per compute unit) being resident together,
+   as they are when no other work holds the device's compute units.
    logits fp32 [T, E], x bf16 [T, H]; out bf16 [T, H]. Of the routing only
-   topk_ids, topk_w (written) and sched are used: sched[28..29] (barrier)
-   and sched[32 ..] (a counter per row and 128-row slab of F) are zero on
-   entry and left zero; sched[30] is set to 1 if the barrier wait gave up
-   after half a second, which makes out invalid.
-   Needs H a multiple of 512 (at most 4096), F a multiple of 256 with
-   (topk + 1) * F <= 16384 and T * (topk + 1) * F / 128 <= 512.
+   topk_ids, topk_w (written) and sched are used: sched[28..29] and
+   sched[32 + 32 g], sched[33 + 32 g] for g < 8 (the barrier's counters) are
+   zero on entry and left zero; sched[30] is set to 1 if the barrier wait
+   gave up after half a second, which makes out invalid.
+   Needs H a multiple of 512 (at most 4096) and F a multiple of 256 with
+   (topk + 1) * F <= 16384.
    workspace: lily_moe_workspace_bytes(dims) bytes.
    Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (T > 4, sizes),
    LILY_ERR_WORKSPACE, LILY_ERR_HIP. */

@@ -10,12 +10,9 @@
 // products on the VALU (bf16 dot2 instructions on the 4-bit values, scale
 // and bias applied to each 32-weight dot product):
 //   phase 0  top-k and softmax of every token (each workgroup, redundantly);
-//   phase A  gate/up: the packed blocks of all rows, in (row, gate/up, slab,
-//            group) order, cut into equal contiguous ranges, one per
-//            workgroup; a range's dot products are summed per 128-row
-//            segment into fp32 partial sums, and the last workgroup to count
-//            in for a (row, slab) adds that slab's partials in workgroup
-//            order into h = bf16(silu(gate) * up);
+//   phase A  gate/up: unit = (row, 8 features): the 8 gate and 8 up weight
+//            rows of those features over all of K, one wavefront per unit,
+//            which forms h = bf16(silu(gate) * up) itself;
 //   one device-wide barrier;
 //   phase B  down and combine: unit = (token, 8 output rows); the unit's
 //            W_down slices of the k + 1 rows times their h, weighted by the
@@ -34,12 +31,10 @@ namespace lily {
 constexpr int kDecThreads = 256;
 constexpr int kDecodeMaxT = 4;       // lily_moe_decode serves T <= this
 constexpr int kDecMaxGrid = 512;     // workgroups: at most one per compute unit and this
-constexpr int kDecBatch = 12;        // phase A blocks loaded per round
+constexpr int kDecASlices = 8;       // phase A slices per lane and weight matrix loaded at once
 constexpr int kDecBRounds = 6;       // phase B rounds per wavefront loaded at once
-constexpr int kDecPieces = 4;        // segments one phase A range may touch
-constexpr int kDecContrib = 8;       // phase A ranges one segment may span
 constexpr int kDecLdsWords = 8192;   // LDS: x rows (phase A) or h rows (phase B), bf16 pairs
-constexpr int kDecXChunks = 4;       // x 16-byte chunks staged per thread: 2 tokens of H <= 4096
+constexpr int kDecXChunks = 8;       // x 16-byte chunks staged per thread: T * H <= 16384
 constexpr int kDecHChunks = kDecLdsWords / 4 / kDecThreads;  // h chunks staged per thread
 constexpr int kDecSums = kDecLdsWords / 16;  // sums of 32 staged values
 constexpr int kDecPiece = 8;         // output rows per phase B unit
@@ -58,12 +53,11 @@ struct DecodeArgs {
     const char* sh_down;
     int32_t* topk_ids;    // [T, k], written by workgroup 0
     float* topk_w;
-    float* pa;            // [segments][kDecContrib][128] phase A partial sums
     uint16_t* h;          // [R][F] bf16
     uint16_t* out;        // [T, H]
-    int32_t* ctr;         // arrivals per (row, slab), ctr_stride apart: zero on entry, left zero
-    int ctr_stride;       // ints between counters (up to a 128-byte line each)
-    int32_t* bar;         // [2] barrier arrivals, exits: zero on entry, left zero
+    int32_t* bar;         // [2] groups arrived, groups exited: zero on entry, left zero
+    int32_t* grp;         // per barrier group: arrivals, exits, kBarLine ints apart; zero on
+                          // entry, left zero
     int32_t* err;         // set to 1 if the barrier wait gave up
 };
 
@@ -152,15 +146,29 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Device-wide barrier: count this workgroup, wait for `target` arrivals.
-// Every global store of the workgroup is complete before it counts. The
-// wait is bounded in time: on a timeout it flags the error and goes on, so
-// no wave can wait forever.
-__device__ __forceinline__ void device_barrier(int32_t* bar, int target, int32_t* err) {
+// Device-wide barrier in two levels. Device-scope atomics on one address
+// are serialised (256 arrivals on one counter took ~7 us), so workgroup w
+// counts in at the counter of its group w % kBarGroups (counters on separate
+// 128-byte lines) and the last of a group counts the group in at `bar`;
+// everyone waits for all groups there. Every global store of the workgroup
+// is complete before it counts. The wait is bounded in time: on a timeout it
+// flags the error and goes on, so no wave can wait forever.
+constexpr int kBarGroups = 8;
+constexpr int kBarLine = 32;  // ints between group counters: one 128-byte line each
+__device__ __forceinline__ int bar_groups(int G) { return G < kBarGroups ? G : kBarGroups; }
+__device__ __forceinline__ int bar_group_size(int G, int g) {
+    return (G - g + kBarGroups - 1) / kBarGroups;
+}
+__device__ __forceinline__ void device_barrier(int32_t* bar, int32_t* grp, int32_t* err) {
+    const int G = gridDim.x, g = blockIdx.x % kBarGroups;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(bar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int prev = __hip_atomic_fetch_add(grp + g * kBarLine, 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == bar_group_size(G, g) - 1)
+            __hip_atomic_fetch_add(bar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int target = bar_groups(G);
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(2);
@@ -173,22 +181,16 @@ __device__ __forceinline__ void device_barrier(int32_t* bar, int target, int32_t
     __syncthreads();
 }
 
-// Phase A ranges: workgroup w of G takes blocks [w NB / G, (w + 1) NB / G)
+// Phase B ranges: workgroup w of G takes units [w NB / G, (w + 1) NB / G)
 // (NB * G < 2^31 on the host's checks).
 __device__ __forceinline__ int range_begin(int w, int nb, int g) { return (unsigned)(w * nb) / (unsigned)g; }
-// The workgroup whose range holds block b (NB >= G, so no range is empty).
-__device__ __forceinline__ int range_owner(int b, int nb, int g) {
-    return (unsigned)((b + 1) * g - 1) / (unsigned)nb;
-}
 
 __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     __shared__ int32_t s_ids[kDecodeMaxT * kMaxTopk];
     __shared__ float s_w[kDecodeMaxT * kMaxTopk];
     __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDecLdsWords];
     __shared__ float s_vsum[kDecSums];  // sums of 32 consecutive staged values
-    __shared__ float s_red[kDecPieces][kPackRows];
     __shared__ float s_bred[kDecThreads / kWave][kDecPiece];
-    __shared__ int s_last[kDecPieces];
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -202,17 +204,10 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     const int nkgF = F / kGroup;       // groups along K of down
     const int nsH = H / kPackRows;     // 128-row slabs of down
 
-    // Phase A range, and the x rows it reads: t_lo and t_lo + 1 (a range
-    // spans at most two tokens). Segment sg = (r * 2 + m) * nsf + slab holds
-    // nkg consecutive blocks (its groups). x is loaded first, to arrive
-    // together with the router logits.
-    const int NB = R * 2 * nsf * nkg;
-    const int b0 = range_begin(wg, NB, G), b1 = range_begin(wg + 1, NB, G);
-    const int seg0 = b0 / nkg;
-    const int t_lo = b0 / ((k + 1) * 2 * nsf * nkg);
-    const int i = tid % kPackRows, hh = tid / kPackRows;
-    const int x_words = (t_lo + 1 < a.T ? 2 : 1) * (H / 2);
-    const Rsrc x_rs = make_rsrc(a.x + (size_t)t_lo * H, x_words * 4);
+    // x of every token, staged in LDS as permuted bf16 pairs, loaded first so
+    // that it arrives together with the router logits.
+    const int x_words = a.T * (H / 2);
+    const Rsrc x_rs = make_rsrc(a.x, x_words * 4);
     u32x4 xr[kDecXChunks];
 #pragma unroll
     for (int n = 0; n < kDecXChunks; ++n)  // chunks past the end read 0
@@ -227,25 +222,12 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         if (c * 4 < x_words) *reinterpret_cast<u32x4*>(s_buf + 4 * c) = permute_chunk(xr[n]);
     }
     __syncthreads();
-    if (tid < x_words / 16) s_vsum[tid] = sum32(s_buf + 16 * tid);
+    for (int q = tid; q < x_words / 16; q += kDecThreads) s_vsum[q] = sum32(s_buf + 16 * q);
     __syncthreads();
     if (wg == 0 && tid < a.T * k) {
         a.topk_ids[tid] = s_ids[tid];
         a.topk_w[tid] = s_w[tid];
     }
-    // Descriptor over segment sg's blocks, and its token.
-    auto seg_rsrc = [&](int sg, int& t) -> Rsrc {
-        const int s = sg % nsf;
-        const int m = (sg / nsf) % 2;
-        const int r = sg / (2 * nsf);
-        t = r / (k + 1);
-        const int j = r - t * (k + 1);
-        const bool sh = (j == k);
-        const int e = sh ? 0 : s_ids[t * k + j];
-        const char* stack = sh ? (m ? a.sh_up : a.sh_gate) : (m ? a.up : a.gate);
-        return make_rsrc(stack + ((size_t)e * nsf + s) * nkg * kPackBlock, nkg * kPackBlock);
-    };
-    const int a_voff_q = (hh * kPackRows + i) * 16, a_voff_s = kPackQ + i * 2;
 
     // Phase B units of this workgroup: wavefront v takes rounds v, v + 4, ...
     // of each. Round rho of a unit: slot j = rho / nq, groups 4 gq .. 4 gq + 3
@@ -274,131 +256,83 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         return load_slice(rs, b_gl * kPackBlock + (b_half * kPackRows + rr) * 16,
                           b_gl * kPackBlock + kPackQ + rr * 2, 0);
     };
-
-    // Loads, in the order they are waited for: the first phase A round, the
-    // first phase B rounds. Rounds past the end are clamped onto valid data
-    // (results unused), so that no load is conditional and the waits can
-    // leave the later loads in flight.
-    float accp[kDecPieces];
-#pragma unroll
-    for (int p = 0; p < kDecPieces; ++p) accp[p] = 0.0f;
+    // The first phase B rounds are loaded right after the first phase A
+    // loads, so that they arrive while phase A computes. Rounds past the end
+    // are clamped onto valid data (results unused).
     Slice pb[kDecBRounds];
     float pw[kDecBRounds];
     int ph[kDecBRounds];
     const int ub_first = ub0 < ub1 ? ub0 : 0;
-    for (int bb = b0; bb < b1; bb += kDecBatch) {
-        const int nb = min(kDecBatch, b1 - bb);
-        // (segment, group) of each block of the round, stepped from the first
-        Slice sl[kDecBatch];
-        int piece[kDecBatch], xoff[kDecBatch];
-        int sg = bb / nkg, g = bb - sg * nkg, t;
-        Rsrc rs = seg_rsrc(sg, t);
+    auto prefetch_b = [&]() {
 #pragma unroll
-        for (int n = 0; n < kDecBatch; ++n) {
-            sl[n] = load_slice(rs, a_voff_q, a_voff_s, g * kPackBlock);
-            piece[n] = sg - seg0;
-            xoff[n] = (t - t_lo) * (H / 2) + g * 32 + hh * 16;
-            if (n + 1 < nb && ++g == nkg) {
-                g = 0;
-                rs = seg_rsrc(++sg, t);
-            }
-        }
-        if (bb == b0) {
-#pragma unroll
-            for (int n = 0; n < kDecBRounds; ++n)
-                pb[n] = b_round(ub_first, min(wv + 4 * n, NRB - 1), pw[n], ph[n]);
-        }
-#pragma unroll
-        for (int n = 0; n < kDecBatch; ++n) {
-            if (n < nb) {
-                const float d = dot_slice(sl[n], s_buf + xoff[n], s_vsum[xoff[n] / 16]);
-#pragma unroll
-                for (int p = 0; p < kDecPieces; ++p)
-                    if (p == piece[n]) accp[p] += d;
-            }
-        }
-    }
+        for (int n = 0; n < kDecBRounds; ++n)
+            pb[n] = b_round(ub_first, min(wv + 4 * n, NRB - 1), pw[n], ph[n]);
+    };
 
-    // Partial sums of the range's segments (the two K halves added), stored
-    // device-coherent.
-    const int npieces = (b1 - 1) / nkg - seg0 + 1;
-    if (hh == 1) {
+    // Phase A: unit u = (row r, features f0 .. f0 + 7): the 8 gate rows and
+    // the 8 up rows of those features over all of K, one wavefront per unit;
+    // units are dealt to workgroup u % G, then to its wavefronts in turn.
+    // Lane l covers feature f0 + l % 8 and the 32-weight slices c = l / 8 +
+    // 8 i of its rows (group c / 2, half c % 2): each load instruction reads
+    // whole 128-byte lines (8 rows x 16 bytes of one block half). The sums
+    // of the 8 lanes of a feature are added by shuffles, and lanes 0-7 form
+    // h = bf16(silu(gate) * up) themselves: no partial sums leave the
+    // wavefront.
+    const int UA = R * (F / 8);
+    const int spr8 = H / 256;  // slices per lane per weight row
+    const int l8 = lane % 8, lc = lane / 8;
+    bool b_loaded = false;
+    for (int u = wg + G * wv; u < UA; u += 4 * G) {
+        const int r = u / (F / 8), f0 = (u - r * (F / 8)) * 8;
+        const int t = r / (k + 1), j = r - t * (k + 1);
+        const bool sh = (j == k);
+        const int e = sh ? 0 : s_ids[t * k + j];
+        const int s = f0 / kPackRows, rr = f0 % kPackRows + l8;
+        const size_t seg = ((size_t)e * nsf + s) * nkg * kPackBlock;
+        const Rsrc rg = make_rsrc((sh ? a.sh_gate : a.gate) + seg, nkg * kPackBlock);
+        const Rsrc ru = make_rsrc((sh ? a.sh_up : a.up) + seg, nkg * kPackBlock);
+        const int voff_q = (lc >> 1) * kPackBlock + ((lc & 1) * kPackRows + rr) * 16;
+        const int voff_s = (lc >> 1) * kPackBlock + kPackQ + rr * 2;
+        const int xbase = t * (H / 2) + (lc >> 1) * 32 + (lc & 1) * 16;
+        float ag = 0.0f, au = 0.0f;
+        for (int i0 = 0; i0 < spr8; i0 += kDecASlices) {
+            // slices past the row's end are clamped onto its last ones
+            // (loaded, not used)
+            Slice sg[kDecASlices], su[kDecASlices];
 #pragma unroll
-        for (int p = 0; p < kDecPieces; ++p) s_red[p][i] = accp[p];
-    }
-    __syncthreads();
-    // slot of this range among the contributors of segment seg0 + p: the
-    // first piece may continue a segment that earlier ranges started
-    const int c0 = wg - range_owner(seg0 * nkg, NB, G);
-    if (hh == 0) {
-#pragma unroll
-        for (int p = 0; p < kDecPieces; ++p)
-            if (p < npieces)
-                __hip_atomic_store(
-                    a.pa + ((size_t)(seg0 + p) * kDecContrib + (p == 0 ? c0 : 0)) * kPackRows + i,
-                    accp[p] + s_red[p][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // Count this range's segments in (thread p counts piece p); the last
-    // contribution to a (row, slab) (of its gate and up segments) builds that
-    // slab of h.
-    if (tid < npieces) {
-        const int sg = seg0 + tid;
-        const int r = sg / (2 * nsf), s = sg % nsf;
-        int total = 0;
-        for (int m = 0; m < 2; ++m) {
-            const int msg = (r * 2 + m) * nsf + s;
-            total += range_owner(msg * nkg + nkg - 1, NB, G) - range_owner(msg * nkg, NB, G) + 1;
-        }
-        int32_t* c = a.ctr + (r * nsf + s) * a.ctr_stride;
-        const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last[tid] = (prev == total - 1);
-        if (prev == total - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    // thread (m, row): the partials of row `row` of the gate (m = 0) or up
-    // segment of each slab this workgroup builds, all loaded before any h
-    // store, added in workgroup order
-    const int m = tid / kPackRows, row = tid % kPackRows;
-    float sums[kDecPieces];
-#pragma unroll
-    for (int p = 0; p < kDecPieces; ++p) {
-        sums[p] = 0.0f;
-        if (p < npieces && s_last[p]) {  // the same in every thread
-            const int sg = seg0 + p;
-            const int r = sg / (2 * nsf), s = sg % nsf;
-            const int msg = (r * 2 + m) * nsf + s;
-            const int nw = range_owner(msg * nkg + nkg - 1, NB, G) - range_owner(msg * nkg, NB, G) + 1;
-            const float* src = a.pa + (size_t)msg * kDecContrib * kPackRows + row;
-            float v[kDecContrib];
-#pragma unroll
-            for (int c = 0; c < kDecContrib; ++c)
-                v[c] = __hip_atomic_load(src + min(c, nw - 1) * kPackRows, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int c = 0; c < kDecContrib; ++c)
-                if (c < nw) sums[p] += v[c];
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < kDecPieces; ++p) {
-        if (p < npieces && s_last[p]) {
-            const int sg = seg0 + p;
-            const int r = sg / (2 * nsf), s = sg % nsf;
-            s_red[m][row] = sums[p];
-            __syncthreads();
-            if (tid < kPackRows / 2) {
-                const float h0 = silu(s_red[0][2 * tid]) * s_red[1][2 * tid];
-                const float h1 = silu(s_red[0][2 * tid + 1]) * s_red[1][2 * tid + 1];
-                __hip_atomic_store(
-                    reinterpret_cast<uint32_t*>(a.h + (size_t)r * F + s * kPackRows) + tid,
-                    pack_bf16x2(h0, h1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < kDecASlices; ++i) {
+                const int soff = min(i0 + i, spr8 - 1) * 4 * kPackBlock;
+                sg[i] = load_slice(rg, voff_q, voff_s, soff);
+                su[i] = load_slice(ru, voff_q, voff_s, soff);
             }
-            __syncthreads();
+            if (!b_loaded) {
+                prefetch_b();
+                b_loaded = true;
+            }
+#pragma unroll
+            for (int i = 0; i < kDecASlices; ++i) {
+                if (i0 + i < spr8) {
+                    const int xo = xbase + (i0 + i) * 128;
+                    const float vs = s_vsum[xo / 16];
+                    ag += dot_slice(sg[i], s_buf + xo, vs);
+                    au += dot_slice(su[i], s_buf + xo, vs);
+                }
+            }
         }
+        ag += __shfl_xor(ag, 8);
+        ag += __shfl_xor(ag, 16);
+        ag += __shfl_xor(ag, 32);
+        au += __shfl_xor(au, 8);
+        au += __shfl_xor(au, 16);
+        au += __shfl_xor(au, 32);
+        const float hv = silu(ag) * au;
+        const float hn = __shfl_down(hv, 1);
+        if (lane < 8 && (lane & 1) == 0)
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h + (size_t)r * F + f0 + lane),
+                               pack_bf16x2(hv, hn), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    device_barrier(a.bar, G, a.err);
+    if (!b_loaded) prefetch_b();
+    device_barrier(a.bar, a.grp, a.err);
 
     // Phase B: out[t, rows] = bf16(sum over slots j of w_j * (W_down_j rows . h_j)).
     // A thread's sum covers output row lane % 8.
@@ -464,23 +398,27 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         __syncthreads();
     }
 
-    // Every workgroup has passed the barrier before it counts here; the last
-    // one clears the counters for the next launch.
-    if (tid == 0 &&
-        __hip_atomic_fetch_add(a.bar + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1) {
-        __hip_atomic_store(a.bar, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.bar + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every workgroup has passed the barrier before it counts out here, in
+    // the same two levels: the last of a group clears the group's counters,
+    // the last group clears `bar` for the next launch.
+    if (tid == 0) {
+        const int g = wg % kBarGroups;
+        int32_t* gc = a.grp + g * kBarLine;
+        if (__hip_atomic_fetch_add(gc + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            bar_group_size(G, g) - 1) {
+            __hip_atomic_store(gc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(gc + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__hip_atomic_fetch_add(a.bar + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                bar_groups(G) - 1) {
+                __hip_atomic_store(a.bar, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.bar + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 
-static long decode_blocks(const lily_moe_dims& d) {
-    return (long)d.T * (d.topk + 1) * 2 * (d.F / kPackRows) * (d.H / kGroup);
-}
-
-// One workgroup per compute unit (at most kDecMaxGrid), each range at least
-// ceil(nkg / (kDecContrib - 1)) blocks long, so that a segment spans at most
-// kDecContrib ranges.
-static int decode_grid(const lily_moe_dims& d) {
+// One workgroup per compute unit, at most kDecMaxGrid.
+static int decode_grid() {
     static int cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -490,38 +428,30 @@ static int decode_grid(const lily_moe_dims& d) {
             n = 0;
         cus[dev] = n > 0 ? n : 1;
     }
-    const long nkg = d.H / kGroup;
-    const long span_min = (nkg + kDecContrib - 2) / (kDecContrib - 1);
-    long g = cus[dev] < kDecMaxGrid ? cus[dev] : kDecMaxGrid;
-    const long lim = decode_blocks(d) / span_min;
-    if (lim < g) g = lim;
-    return (int)(g > 0 ? g : 1);
+    return cus[dev] < kDecMaxGrid ? cus[dev] : kDecMaxGrid;
 }
 
+// h, bf16 [T (k + 1), F].
 size_t decode_workspace_bytes(const lily_moe_dims& d) {
     if (d.T > kDecodeMaxT) return 0;
-    const size_t R = (size_t)d.T * (d.topk + 1);
-    const size_t segments = R * 2 * (d.F / kPackRows);
-    return segments * kDecContrib * kPackRows * sizeof(float) + R * d.F * sizeof(uint16_t);
+    return (size_t)d.T * (d.topk + 1) * d.F * sizeof(uint16_t);
 }
+
+constexpr int kDecMaxH = 4096;  // x of kDecodeMaxT tokens fills the LDS staging area
+static_assert(kDecodeMaxT * kDecMaxH / 2 <= kDecLdsWords, "x staging");
+static_assert(kDecodeMaxT * kDecMaxH / 2 <= kDecXChunks * 4 * kDecThreads, "x chunks");
 
 int decode_supported(const lily_moe_dims& d) {
     if (d.T > kDecodeMaxT)
         return set_error(LILY_ERR_UNSUPPORTED, "T = %d; lily_moe_decode serves T <= %d", d.T,
                          kDecodeMaxT);
-    if (d.H % (2 * kDecThreads) || d.H > kDecXChunks * 4 * kDecThreads)
+    if (d.H % (2 * kDecThreads) || d.H > kDecMaxH)
         return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 512, at most %d",
-                         d.H, kDecXChunks * 4 * kDecThreads);
+                         d.H, kDecMaxH);
     if (d.F % (4 * kGroup) || (long)(d.topk + 1) * d.F > 2L * kDecLdsWords)
         return set_error(LILY_ERR_UNSUPPORTED,
                          "F = %d must be a multiple of 256 with (topk + 1) * F <= %d", d.F,
                          2 * kDecLdsWords);
-    const long R = (long)d.T * (d.topk + 1);
-    if (R * (d.F / kPackRows) > kTileCounters)
-        return set_error(LILY_ERR_UNSUPPORTED, "T * (topk + 1) * F / 128 = %ld exceeds %d",
-                         R * (d.F / kPackRows), kTileCounters);
-    if (decode_blocks(d) * kDecMaxGrid >= (1L << 31))
-        return set_error(LILY_ERR_UNSUPPORTED, "decode: %ld blocks are too many", decode_blocks(d));
     return LILY_OK;
 }
 
@@ -544,27 +474,13 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
     a.sh_down = static_cast<const char*>(w.sh_down);
     a.topk_ids = r.topk_ids;
     a.topk_w = r.topk_w;
-    a.pa = static_cast<float*>(workspace);
-    const size_t segments = (size_t)d.T * (d.topk + 1) * 2 * (d.F / kPackRows);
-    a.h = reinterpret_cast<uint16_t*>(a.pa + segments * kDecContrib * kPackRows);
+    a.h = static_cast<uint16_t*>(workspace);
     a.out = out;
-    // Counters on lines of their own where the sched array has room: device
-    // scope atomics on one line are serialised.
-    a.ctr = r.sched + kQueueInts;
-    const long n_ctr = (long)d.T * (d.topk + 1) * (d.F / kPackRows);
-    a.ctr_stride = 1;
-    while (a.ctr_stride < 32 && 2 * a.ctr_stride * n_ctr <= kSchedInts - kQueueInts)
-        a.ctr_stride *= 2;
     a.bar = r.sched + kDecodeBarrier;
+    a.grp = r.sched + kQueueInts;
     a.err = r.sched + kDecodeBarrier + 2;
-    // A phase A range touches at most kDecPieces segments and two tokens; a
-    // segment spans at most kDecContrib ranges.
-    const long nb = decode_blocks(d), g = decode_grid(d), nkg = d.H / kGroup;
-    const long span_max = (nb + g - 1) / g, span_min = nb / g;
-    if (span_min < 1 || (span_max + nkg - 1) / nkg + 1 > kDecPieces || span_max > nb / d.T ||
-        (nkg + span_min - 1) / span_min + 1 > kDecContrib)
-        return set_error(LILY_ERR_UNSUPPORTED, "decode ranges of %ld..%ld blocks over %ld groups",
-                         span_min, span_max, nkg);
+    static_assert(kQueueInts + kBarGroups * kBarLine <= kSchedInts, "barrier group counters");
+    const int g = decode_grid();
     // At most one workgroup per compute unit, each needing a fraction of a
     // compute unit's registers and LDS: all are resident at once, which the
     // device-wide barrier relies on.
