@@ -54,6 +54,16 @@ __global__ void __launch_bounds__(kTopkThreads) route_topk_kernel(
     }
 }
 
+// Workgroup barrier that waits for this thread's LDS accesses only. Global
+// stores stay in flight: nothing in route_finish reads back what another
+// thread of it stored (__syncthreads would wait for every store to reach
+// memory first, a round trip per barrier).
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront: DPP shifts inside
 // each row of 16 lanes (out-of-row sources read 0), then the row totals
 // from lanes 15, 31, 47 added to the later rows. No LDS traffic.
@@ -87,7 +97,7 @@ __device__ __forceinline__ void block_exclusive_scan(const int (&v)[NV], int (&e
 #pragma unroll
         for (int i = 0; i < NV; ++i) s_wsum[i * kFinishWaves + wave] = inc[i];
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int ws = wave_inclusive_scan(lane < kFinishWaves ? s_wsum[i * kFinishWaves + lane] : 0);
@@ -95,7 +105,7 @@ __device__ __forceinline__ void block_exclusive_scan(const int (&v)[NV], int (&e
         tot[i] = __builtin_amdgcn_readlane(ws, kFinishWaves - 1);
         ex[i] = base + inc[i] - v[i];
     }
-    __syncthreads();
+    lds_sync();
 }
 
 __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
@@ -139,19 +149,23 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     const bool lane_in_chunk = lane < cpairs;
 
     // Pass 1: rows per expert in each span (integer LDS atomics: the totals
-    // do not depend on their order).
+    // do not depend on their order). When the span is one batch, its ids
+    // stay in registers for pass 2.
+    const bool one_batch = p_end - p_begin <= cpairs * kBatch;
+    int ids0[kBatch];
     for (int c0 = p_begin; c0 < p_end; c0 += cpairs * kBatch) {
         int ids[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const int p = c0 + b * cpairs + lane;
             ids[b] = (lane_in_chunk && p < p_end) ? topk_ids[p] : -1;
+            ids0[b] = ids[b];
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b)
             if (ids[b] >= 0) atomicAdd(&hist[wave][ids[b]], 1);
     }
-    __syncthreads();
+    lds_sync();
 
     // Per-expert totals, and each span's base inside its expert.
     for (int e = tid; e < E; e += kFinishThreads) {
@@ -165,7 +179,7 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
         s_off[e] = run;
         s_bst[e] = (run + M - 1) / M;
     }
-    __syncthreads();
+    lds_sync();
 
     // Exclusive scans over the experts, one expert per thread (E <= 512 <
     // 1024 threads): rows (s_off), blocks (s_bst), full blocks (s_fst), and
@@ -202,7 +216,7 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
         }
     }
     for (int i = tid; i < kSchedInts; i += kFinishThreads) sched[i] = 0;
-    __syncthreads();
+    lds_sync();
 
     for (int e = tid; e <= E; e += kFinishThreads) offsets[e] = s_off[e];
     const int nb = s_bst[E];
@@ -233,7 +247,7 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const int p = c0 + b * cpairs + lane;
-            ids[b] = (lane_in_chunk && p < p_end) ? topk_ids[p] : -1;
+            ids[b] = one_batch ? ids0[b] : (lane_in_chunk && p < p_end) ? topk_ids[p] : -1;
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
