@@ -121,6 +121,11 @@ typedef struct {
                               rows) in block order, then each expert's last,
                               partial block by descending size class
                               ceil(4 rows / tile_m), ties in expert order;
+   block_info int32 [lily_moe_max_blocks(dims)][4]
+                              the same schedule resolved: entry i holds
+                              (expert, first row, rows, block) of block
+                              block_order[i], so that a GEMM workgroup
+                              learns a block's extent with one load;
    sched int32 [LILY_SCHED_INTS]
                               work-queue and split-K tile counters of the
                               grouped GEMMs. Zero them once after
@@ -141,6 +146,7 @@ typedef struct {
     int32_t* num_blocks;
     int32_t* block_order;
     int32_t* sched;
+    int32_t* block_info;
 } lily_moe_routing;
 
 /* Host, pure. Capacity of the block map: ceil(P / tile_m) + min(E, P).

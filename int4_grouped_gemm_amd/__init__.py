@@ -47,7 +47,8 @@ class LilyMoeWeights(ctypes.Structure):
 
 
 ROUTING_FIELDS = ("topk_ids", "topk_w", "counts", "offsets", "sorted_pairs", "pair_rows",
-                  "block_expert", "block_row0", "num_blocks", "block_order", "sched")
+                  "block_expert", "block_row0", "num_blocks", "block_order", "sched",
+                  "block_info")
 
 
 class LilyMoeRouting(ctypes.Structure):
@@ -190,6 +191,7 @@ class Routing:
     num_blocks: torch.Tensor
     block_order: torch.Tensor
     sched: torch.Tensor
+    block_info: torch.Tensor
 
     def c(self) -> LilyMoeRouting:
         if getattr(self, "_c", None) is None:
@@ -314,7 +316,8 @@ def alloc_routing(d: LilyMoeDims, device="cuda") -> Routing:
                    sorted_pairs=torch.empty(P, **i32), pair_rows=torch.empty(P, **i32),
                    block_expert=torch.empty(mb, **i32), block_row0=torch.empty(mb, **i32),
                    num_blocks=torch.empty(1, **i32), block_order=torch.empty(mb, **i32),
-                   sched=torch.zeros(LILY_SCHED_INTS, **i32))
+                   sched=torch.zeros(LILY_SCHED_INTS, **i32),
+                   block_info=torch.empty((mb, 4), **i32))
 
 
 def alloc_workspace(d: LilyMoeDims, device="cuda") -> torch.Tensor:

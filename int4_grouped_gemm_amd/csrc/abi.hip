@@ -94,6 +94,7 @@ static int check_routing(const lily_moe_routing* r) {
     REQUIRE_PTR(r->num_blocks);
     REQUIRE_PTR(r->block_order);
     REQUIRE_PTR(r->sched);
+    REQUIRE_PTR(r->block_info);
     return LILY_OK;
 }
 

@@ -22,8 +22,9 @@
 // The grid is persistent (as many workgroups as fit on the device) and
 // takes tiles from eight work queues, one per XCD: queue x owns the blocks
 // x, x + 8, ... of the schedule (the shared expert's blocks, then the
-// routed blocks in block_order, largest first), with their n-tiles
-// consecutive so that they meet the same A rows in one L2.
+// routed blocks in block_order, largest first, read resolved from
+// block_info), with their n-tiles consecutive so that they meet the same A
+// rows in one L2.
 //
 // LDS A tiles are [rows][64] bf16 with the 16-byte chunks of each row
 // XOR-swizzled by ((row >> 1) & 7). The LDS has 64 four-byte banks, so a
@@ -44,11 +45,8 @@ struct GemmArgs {
     const char* w[2];               // packed routed stacks: gate/up -> gate, up; down -> W_down twice
     const char* sw[2];              // packed shared-expert stacks, same roles
     int N, K;
-    const int32_t* block_expert;
-    const int32_t* block_row0;
-    const int32_t* block_order;
+    const int4* block_info;         // per schedule position: expert, first row, rows, block
     const int32_t* num_blocks;
-    const int32_t* offsets;
     int shared_blocks;  // ceil(T / BM)
     int P, T;
     int32_t* sched;     // kXcds queue counters, then the finished-workgroup counter
@@ -87,11 +85,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 // is the 16-byte chunk 4h + s of its row.
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
-// Workgroups whose own queue is empty take items from the other queues.
-// Off: at the end of a launch the idle workgroups of drained queues would
-// all contend for the few remaining counters, which costs more than the
-// imbalance between queues.
-constexpr bool kSteal = false;
 
 template <bool GATED>
 struct GemmShape {
@@ -162,7 +155,9 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t lane_off, uint32
 // workgroup. Consecutive calls alternate between two LDS slots, so a slot is
 // rewritten only after the barrier of the following call, which every
 // wavefront reaches after reading it. Only LDS is waited for: DMA loads in
-// flight stay in flight.
+// flight stay in flight. (Taking the ticket one item ahead, to hide the
+// atomic's latency, was slower: at the end of a launch the reserved items
+// wait on busy workgroups while others idle.)
 __device__ __forceinline__ int grab(int32_t* ctr, int* s_slot, int& toggle) {
     int* slot = s_slot + toggle;
     toggle ^= 1;
@@ -378,9 +373,12 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
                 }
             }
         // The partials are device-coherent stores (they write through the
-        // XCD's L2), complete before the barrier (__syncthreads waits for
-        // them), and read back with device-coherent loads: no fence, which on
-        // this GPU would write back the whole L2.
+        // XCD's L2). Every wavefront waits for its own stores to complete
+        // before the barrier (a workgroup barrier alone does not wait for
+        // global stores), so all of them are complete before the chunk
+        // counts in; they are read back with device-coherent loads. No
+        // fence, which on this GPU would write back the whole L2.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0)
             *s_flag = __hip_atomic_fetch_add(args.tile_ctr + lp.tile, 1, __ATOMIC_RELAXED,
@@ -443,15 +441,17 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
 
     // Work queue x = blockIdx.x % 8: with round-robin dispatch of workgroups
     // over the XCDs all of a queue's workgroups share one L2. A workgroup
-    // drains its own queue, then takes what is left in the others (in
-    // order x + 1, x + 2, ...); each item is taken exactly once through its
+    // drains its own queue; each item is taken exactly once through the
     // queue's counter. Correctness does not depend on the XCD mapping.
+    // (Taking items from other queues once the own queue is empty costs
+    // more than the imbalance it removes: the idle workgroups all contend
+    // for the last counters.)
     const int n_tiles = args.N / BN;
     const int nb_total = args.shared_blocks + args.num_blocks[0];
     const int n_slabs = args.N / kPackRows;
     const size_t slab_bytes = (size_t)(args.K / 64) * kPackBlock;
-    int cq = blockIdx.x % kXcds;
-    int tried = 0, toggle = 0;
+    const int cq = blockIdx.x % kXcds;
+    int toggle = 0;
 
     // Items of queue q: its blocks q, q + 8, ... times the n-tiles times the
     // K chunks (the chunks of a tile consecutive).
@@ -459,10 +459,10 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
         return (nb_total > q ? (nb_total - q + kXcds - 1) / kXcds : 0) * n_tiles * args.kc;
     };
     // Takes the next item of queue cq (one atomic) and resolves its rows,
-    // expert and load plan; it.valid = false if the queue is empty.
+    // expert and load plan (one load of block_info); it.valid = false if the
+    // queue is empty.
     auto take = [&](Item<MI>& it) {
         it.valid = false;
-        if (tried >= kXcds) return;
         const int c = grab(args.sched + cq, s_slot, toggle);
         if (c >= items_of(cq)) return;
         {
@@ -471,20 +471,19 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
             const int vb = cq + kXcds * (ct / n_tiles);
             const int nt = ct % n_tiles;
             it.tile = vb * n_tiles + nt;
-            int r_end, e = 0;
+            int e = 0;
             bool shared;
             if (vb < args.shared_blocks) {
                 it.r0 = args.P + vb * BM;
-                r_end = args.P + args.T;
+                it.rows = min(BM, args.P + args.T - it.r0);
                 shared = true;
             } else {
-                const int blk = args.block_order[vb - args.shared_blocks];
-                e = args.block_expert[blk];
-                it.r0 = args.block_row0[blk];
-                r_end = args.offsets[e + 1];
+                const int4 info = args.block_info[vb - args.shared_blocks];
+                e = info.x;
+                it.r0 = info.y;
+                it.rows = info.z;
                 shared = false;
             }
-            it.rows = min(BM, r_end - it.r0);
             it.mia = min(MI, (it.rows + 31) / 32);
             it.prefetched = false;
             it.n0 = nt * BN;
@@ -515,22 +514,11 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
             return;
         }
     };
-    // Once the own queue is empty: try the next queues in turn (when
-    // kSteal). Every decision here follows a value that grab() broadcast
-    // through LDS, so all wavefronts take the same path and meet at the
-    // same barriers.
-    auto steal = [&](Item<MI>& it) {
-        while (kSteal && !it.valid) {
-            cq = (cq + 1) % kXcds;
-            if (++tried >= kXcds) return;
-            take(it);
-        }
-    };
-
+    // Every decision follows a value that grab() sent through LDS, so all
+    // wavefronts take the same path and meet at the same barriers.
     const uint32_t smem_addr = (uint32_t)(size_t)smem;
     Item<MI> cur;
     take(cur);
-    steal(cur);
     while (cur.valid) {
         Item<MI> nxt;
         // After the k-loop (every wavefront is done with the LDS stages):
@@ -552,7 +540,6 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
         else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, cur, wave, s_slot + 2, prep);
         else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, cur, wave, s_slot + 2, prep);
         else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, cur, wave, s_slot + 2, prep);
-        steal(nxt);  // after the stores: only the last items of a workgroup get here with nothing
         cur = nxt;
     }
 
@@ -670,11 +657,8 @@ ForwardWorkspace forward_workspace_split(const lily_moe_dims& d, void* ws) {
 static GemmArgs routing_args(const lily_moe_dims& d, const lily_moe_routing& r) {
     GemmArgs g{};
     g.topk = d.topk;
-    g.block_expert = r.block_expert;
-    g.block_row0 = r.block_row0;
-    g.block_order = r.block_order;
+    g.block_info = reinterpret_cast<const int4*>(r.block_info);
     g.num_blocks = r.num_blocks;
-    g.offsets = r.offsets;
     g.P = d.T * d.topk;
     g.T = d.T;
     return g;

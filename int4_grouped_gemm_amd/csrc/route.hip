@@ -25,8 +25,9 @@
 //                 atomic: deterministic and bit-exact. It also writes the
 //                 schedule of the grouped GEMMs (block_order: full blocks in
 //                 block order, then each expert's last, partial block by
-//                 descending size class, ties in expert order) and clears
-//                 their work-queue counters.
+//                 descending size class, ties in expert order), the same
+//                 schedule resolved to (expert, first row, rows, block) in
+//                 block_info, and clears their work-queue counters.
 // For small T the top-k runs inside route_finish and the route is one launch.
 #include "common.hpp"
 #include "topk.hpp"
@@ -114,7 +115,8 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_rows, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ block_row0, int32_t* __restrict__ num_blocks,
-    int32_t* __restrict__ block_order, int32_t* __restrict__ sched) {
+    int32_t* __restrict__ block_order, int32_t* __restrict__ sched,
+    int32_t* __restrict__ block_info) {
     __shared__ int32_t hist[kFinishWaves][kMaxExperts];    // rows per span, then cursors
     __shared__ uint32_t cmask[kFinishWaves][kMaxExperts];  // tokens of a chunk, per expert
     __shared__ int32_t s_off[kMaxExperts + 1];             // row offsets
@@ -208,7 +210,11 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
             s_off[e] = ex_rows;
             s_bst[e] = ex_blks;
             s_fst[e] = ex_full;
-            if (rem_e > 0) block_order[cls_rank] = ex_blks + full_e;
+            if (rem_e > 0) {
+                block_order[cls_rank] = ex_blks + full_e;
+                *reinterpret_cast<int4*>(block_info + 4 * cls_rank) =
+                    make_int4(e, ex_rows + full_e * M, rem_e, ex_blks + full_e);
+            }
         }
         if (e == 0) {
             s_off[E] = tot_rows;
@@ -232,7 +238,11 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
         block_expert[b] = lo;
         block_row0[b] = s_off[lo] + (b - s_bst[lo]) * M;
         const int j = b - s_bst[lo];
-        if (j < (s_off[lo + 1] - s_off[lo]) / M) block_order[s_fst[lo] + j] = b;
+        if (j < (s_off[lo + 1] - s_off[lo]) / M) {
+            block_order[s_fst[lo] + j] = b;
+            *reinterpret_cast<int4*>(block_info + 4 * (s_fst[lo] + j)) =
+                make_int4(lo, s_off[lo] + j * M, M, b);
+        }
     }
 
     // Pass 2: stable positions. The k experts of a token are distinct, so
@@ -283,7 +293,7 @@ int launch_route(const lily_moe_dims& d, const float* logits, const lily_moe_rou
     hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(kFinishThreads), 0, stream, logits, d.T,
                        d.E, d.topk, d.tile_m, fused, r.topk_ids, r.topk_w, r.counts, r.offsets,
                        r.sorted_pairs, r.pair_rows, r.block_expert, r.block_row0, r.num_blocks,
-                       r.block_order, r.sched);
+                       r.block_order, r.sched, r.block_info);
     return check_launch("route_finish");
 }
 

@@ -30,7 +30,7 @@ def route_gpu(d: L.LilyMoeDims, logits: np.ndarray, device="cuda"):
 def routing_to_host(r: L.Routing) -> dict:
     out = {n: getattr(r, n).cpu().numpy() for n in L.ROUTING_FIELDS}
     nb = int(out["num_blocks"][0])
-    for key in ("block_expert", "block_row0", "block_order"):
+    for key in ("block_expert", "block_row0", "block_order", "block_info"):
         out[key] = out[key][:nb]
     return out
 
@@ -59,6 +59,10 @@ def compare_routing(gpu: dict, ref: dict, tile_m: int = None) -> None:
     if tile_m is not None:
         want = expected_block_order(ref, tile_m)
         assert np.array_equal(gpu["block_order"], want), "block_order"
+        be, br0 = np.asarray(ref["block_expert"]), np.asarray(ref["block_row0"])
+        rows = np.minimum(tile_m, np.asarray(ref["offsets"])[be[want] + 1] - br0[want])
+        info = np.stack([be[want], br0[want], rows, want], axis=1).astype(np.int32)
+        assert np.array_equal(gpu["block_info"].reshape(-1, 4), info.reshape(-1, 4)), "block_info"
         assert not np.any(gpu["sched"]), "route must leave the GEMM queue counters zero"
 
 
