@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--router", action="store_true",
                     help="start each step from x: the router projection x.Wr^T (lily_moe_router) "
                          "computes the logits inside the timed step")
+    ap.add_argument("--route-host", action="store_true",
+                    help="ablation: route with lily_moe_route_host (histogram, scan, scatter and "
+                         "block map on the host after a stream synchronisation)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of layer 0 the CPU oracle computes for the baseline")
@@ -129,7 +132,8 @@ def main():
         calls = []
         if args.router:
             calls.append(lambda: L.lily_moe_router(d, routers[layer], x, logits[layer], stream))
-        calls += [lambda: L.lily_moe_route(d, logits[layer], routing, stream),
+        route = L.lily_moe_route_host if args.route_host else L.lily_moe_route
+        calls += [lambda: route(d, logits[layer], routing, stream),
                   lambda: L.lily_moe_gate_up(d, w, x, routing, ws, stream),
                   lambda: L.lily_moe_down(d, w, routing, ws, stream),
                   lambda: L.lily_moe_combine(d, routing, ws, out, stream)]
@@ -214,6 +218,8 @@ def main():
             "routing": "logits N(0,1) + per-expert Zipf(1.1) log-bias" if cfg.zipf
                        else "logits N(0,1)",
             "weights": "int4 q~U{0..15}, bf16 scale~U(0.005,0.02), bf16 bias~N(0,0.01)",
+            "route": "host-synchronised (lily_moe_route_host)" if args.route_host
+                     else "GPU-resident (lily_moe_route)",
         },
         "layer": {
             "mfma_frac": round(layer_flops / step_s / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),

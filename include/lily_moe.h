@@ -198,6 +198,19 @@ int lily_moe_router(const lily_moe_dims* dims, const uint16_t* w_router, const u
 int lily_moe_route(const lily_moe_dims* dims, const float* logits,
                    const lily_moe_routing* routing, void* stream);
 
+/* Ablation twin of lily_moe_route with CPU-synchronised routing (the Lily
+   articles, section "Prefill", credit GPU-resident routing with a large
+   prefill speed-up over this): the top-k and softmax run on the GPU as in
+   lily_moe_route; the ids are then copied to the host, the stream is
+   synchronised, the host computes the histogram, scan, stable scatter,
+   block map and GEMM schedule with the same definitions, uploads them and
+   zeroes sched, and the stream is synchronised again before returning.
+   The routing written is bit-identical to lily_moe_route's. Blocks the
+   calling thread; allocates host memory only. Same arguments and errors as
+   lily_moe_route. */
+int lily_moe_route_host(const lily_moe_dims* dims, const float* logits,
+                        const lily_moe_routing* routing, void* stream);
+
 /* Expert computation of one MoE layer from a routing produced by
    lily_moe_route with the same dims: grouped gate/up GEMM with the int4 ->
    bf16 dequantisation fused into the tile loads, SwiGLU, grouped down GEMM,

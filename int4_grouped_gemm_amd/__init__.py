@@ -24,7 +24,8 @@ LILY_ERR_WORKSPACE = -3
 LILY_ERR_HIP = -4
 
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
-           "lily_w4_pack", "lily_moe_router", "lily_moe_route", "lily_moe_forward", "lily_moe_gate_up",
+           "lily_w4_pack", "lily_moe_router", "lily_moe_route", "lily_moe_route_host",
+           "lily_moe_forward", "lily_moe_gate_up",
            "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_residual_norm",
            "lily_last_error")
 LILY_SCHED_INTS = 1056
@@ -90,6 +91,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_moe_route.restype = ctypes.c_int
     lib.lily_moe_route.argtypes = [P(LilyMoeDims), ctypes.c_void_p, P(LilyMoeRouting),
                                    ctypes.c_void_p]
+    lib.lily_moe_route_host.restype = ctypes.c_int
+    lib.lily_moe_route_host.argtypes = [P(LilyMoeDims), ctypes.c_void_p, P(LilyMoeRouting),
+                                        ctypes.c_void_p]
     lib.lily_moe_forward.restype = ctypes.c_int
     lib.lily_moe_forward.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
                                      P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p,
@@ -240,6 +244,14 @@ def lily_moe_route(d: LilyMoeDims, logits, routing: Routing, stream=None) -> Non
     lib = load()
     rc = lib.lily_moe_route(ctypes.byref(d), _ptr(logits), ctypes.byref(routing.c()),
                             _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_route_host(d: LilyMoeDims, logits, routing: Routing, stream=None) -> None:
+    """The CPU-synchronised twin of lily_moe_route (blocks the calling thread)."""
+    lib = load()
+    rc = lib.lily_moe_route_host(ctypes.byref(d), _ptr(logits), ctypes.byref(routing.c()),
+                                 _stream(stream))
     _check(rc, lib)
 
 

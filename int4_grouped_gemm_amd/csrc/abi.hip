@@ -25,6 +25,8 @@ int check_launch(const char* what) {
 
 int launch_route(const lily_moe_dims& d, const float* logits, const lily_moe_routing& r,
                  hipStream_t stream);
+int launch_route_host(const lily_moe_dims& d, const float* logits, const lily_moe_routing& r,
+                      hipStream_t stream);
 int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
                    const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
                    hipStream_t stream);
@@ -204,6 +206,16 @@ int lily_moe_route(const lily_moe_dims* dims, const float* logits,
     rc = check_routing(routing);
     if (rc) return rc;
     return launch_route(*dims, logits, *routing, reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_route_host(const lily_moe_dims* dims, const float* logits,
+                        const lily_moe_routing* routing, void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    REQUIRE_PTR(logits);
+    rc = check_routing(routing);
+    if (rc) return rc;
+    return launch_route_host(*dims, logits, *routing, reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,

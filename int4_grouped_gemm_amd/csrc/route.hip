@@ -280,6 +280,15 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
     }
 }
 
+// Top-k and softmax of every token only (the host-synchronised route).
+int launch_topk_only(const lily_moe_dims& d, const float* logits, const lily_moe_routing& r,
+                     hipStream_t stream) {
+    const int grid = (d.T + kTopkTokensPerBlock - 1) / kTopkTokensPerBlock;
+    hipLaunchKernelGGL(route_topk_kernel, dim3(grid), dim3(kTopkThreads), 0, stream, logits, d.T,
+                       d.E, d.topk, r.topk_ids, r.topk_w);
+    return check_launch("route_topk");
+}
+
 int launch_route(const lily_moe_dims& d, const float* logits, const lily_moe_routing& r,
                  hipStream_t stream) {
     const int fused = d.T <= kFusedRouteMaxT;

@@ -109,6 +109,21 @@ def test_route_rejects_pointers(lib):
     assert lib.lily_moe_route(None, FAKE, ctypes.byref(routing()), None) == L.LILY_ERR_INVALID_ARG
 
 
+def test_route_host_rejects(lib):
+    """The host-synchronised twin validates like lily_moe_route, before any
+    device work."""
+    d = good_dims()
+    assert lib.lily_moe_route_host(ctypes.byref(d), None, ctypes.byref(routing()), None) == \
+        L.LILY_ERR_INVALID_ARG
+    assert "logits" in lib.lily_last_error().decode()
+    for n in L.ROUTING_FIELDS:
+        assert lib.lily_moe_route_host(ctypes.byref(d), FAKE, ctypes.byref(routing(**{n: None})),
+                                       None) == L.LILY_ERR_INVALID_ARG
+        assert n in lib.lily_last_error().decode()
+    assert lib.lily_moe_route_host(ctypes.byref(good_dims(E=513)), FAKE, ctypes.byref(routing()),
+                                   None) == L.LILY_ERR_UNSUPPORTED
+
+
 def test_forward_rejects(lib):
     assert call_forward(lib, good_dims(tile_m=48)) == L.LILY_ERR_UNSUPPORTED
     assert call_forward(lib, good_dims(H=192)) == L.LILY_ERR_UNSUPPORTED

@@ -86,6 +86,46 @@ def test_route_deterministic():
         assert np.array_equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("case", [c for c in ROUTE_CASES if c[0] in
+                                  ("tiny", "prefill512", "zipf2048_m128", "decode_T1", "m1",
+                                   "E512_k64", "odd_T")], ids=lambda c: c[0])
+def test_route_host_twin(case):
+    """lily_moe_route_host (the CPU-synchronised twin) writes the oracle's
+    routing bit for bit, the same as lily_moe_route, and the forward after
+    it gives the forward after the GPU route bit for bit."""
+    name, T, E, k, M, src = case
+    _flush(f"route_host case {name}: T={T} E={E} k={k} M={M}")
+    if src is None:
+        lg = np.random.default_rng([T, E, k]).standard_normal((T, E)).astype(np.float32)
+    else:
+        lg = S.router_logits(S.CONFIGS[src], T=T)
+    d = L.dims(T, 256, 128, E, k, M)
+    r = L.alloc_routing(d)
+    r.sched.fill_(7)  # the twin must clear the GEMM counters itself
+    L.lily_moe_route_host(d, torch.from_numpy(lg).cuda(), r)
+    torch.cuda.synchronize()
+    G.compare_routing(G.routing_to_host(r), oracle.route(lg, k, M), M)
+    gpu = G.routing_to_host(G.route_gpu(d, lg))
+    host = G.routing_to_host(r)
+    for key in L.ROUTING_FIELDS:
+        assert np.array_equal(gpu[key], host[key]), key
+
+
+def test_route_host_twin_forward():
+    cfg = S.CONFIGS["prefill512"]
+    lw = S.layer_weights(cfg, 0)
+    x = S.activations(cfg, 0)
+    lg = S.router_logits(cfg, 0, 0)
+    d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, 64)
+    w = L.weights_from_host(lw)
+    xd = G.to_dev_bits(x)
+    a = G.from_dev_bits(G.forward_gpu(d, w, xd, G.route_gpu(d, lg)))
+    r = L.alloc_routing(d)
+    L.lily_moe_route_host(d, torch.from_numpy(lg).cuda(), r)
+    b = G.from_dev_bits(G.forward_gpu(d, w, xd, r))
+    assert np.array_equal(a, b), "forward after the host route differs"
+
+
 # ------------------------------------------------------------------- forward
 
 def _layer_case(cfg, tile_m, tokens=None, layer=0, seed=0):
