@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--route-host", action="store_true",
                     help="ablation: route with lily_moe_route_host (histogram, scan, scatter and "
                          "block map on the host after a stream synchronisation)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="ablation: lily_moe_dequant (bf16 weights of the used experts to HBM) "
+                         "then lily_moe_forward_bf16 (the same GEMMs on bf16 tiles); tile_m 32 "
+                         "or 64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of layer 0 the CPU oracle computes for the baseline")
@@ -81,6 +85,10 @@ def stage_work(cfg, P):
         "gate_up": ("mfma", 2.0 * rows * cfg.H * 2 * cfg.F),
         "down": ("mfma", 2.0 * rows * cfg.F * cfg.H),
         "combine": ("hbm", rows * cfg.H * 4 + cfg.T * cfg.H * 2 + P * 8),
+        # unfused twin: the packed weights of every expert read (upper bound:
+        # only used ones are) and their bf16 written; then both GEMMs
+        "dequant": ("hbm", (cfg.E + 1) * 3 * cfg.H * cfg.F * (0.5625 + 2.0)),
+        "forward_bf16": ("mfma", 2.0 * rows * cfg.H * 3 * cfg.F),
     }
 
 
@@ -120,11 +128,16 @@ def main():
     routing = L.alloc_routing(d, dev)
     ws = L.alloc_workspace(d, dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+    if args.unfused and args.tile_m not in (32, 64):
+        sys.exit("--unfused needs --tile-m 32 or 64")
+    bf16w = L.alloc_bf16_weights(d, dev) if args.unfused else None
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    stages = (("router",) if args.router else ()) + ("route", "gate_up", "down", "combine")
+    stages = (("router",) if args.router else ()) + (
+        ("route", "dequant", "forward_bf16") if args.unfused else
+        ("route", "gate_up", "down", "combine"))
 
     def step(i, ev=None):
         layer = i % args.layers
@@ -133,10 +146,15 @@ def main():
         if args.router:
             calls.append(lambda: L.lily_moe_router(d, routers[layer], x, logits[layer], stream))
         route = L.lily_moe_route_host if args.route_host else L.lily_moe_route
-        calls += [lambda: route(d, logits[layer], routing, stream),
-                  lambda: L.lily_moe_gate_up(d, w, x, routing, ws, stream),
-                  lambda: L.lily_moe_down(d, w, routing, ws, stream),
-                  lambda: L.lily_moe_combine(d, routing, ws, out, stream)]
+        calls.append(lambda: route(d, logits[layer], routing, stream))
+        if args.unfused:
+            calls += [lambda: L.lily_moe_dequant(d, w, routing, bf16w, stream),
+                      lambda: L.lily_moe_forward_bf16(d, bf16w, x, routing, out, ws,
+                                                      stream=stream)]
+        else:
+            calls += [lambda: L.lily_moe_gate_up(d, w, x, routing, ws, stream),
+                      lambda: L.lily_moe_down(d, w, routing, ws, stream),
+                      lambda: L.lily_moe_combine(d, routing, ws, out, stream)]
         for j, call in enumerate(calls):
             if ev is not None:
                 ev[j].record(stream)
@@ -220,6 +238,9 @@ def main():
             "weights": "int4 q~U{0..15}, bf16 scale~U(0.005,0.02), bf16 bias~N(0,0.01)",
             "route": "host-synchronised (lily_moe_route_host)" if args.route_host
                      else "GPU-resident (lily_moe_route)",
+            "dequant": "unfused: bf16 weights through HBM (lily_moe_dequant + "
+                       "lily_moe_forward_bf16)" if args.unfused
+                       else "fused into the grouped GEMM",
         },
         "layer": {
             "mfma_frac": round(layer_flops / step_s / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),

@@ -247,6 +247,31 @@ int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
 int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
                      void* workspace, size_t workspace_bytes, uint16_t* out, void* stream);
 
+/* Ablation twin of the fused dequantisation (the Lily articles, section
+   "Prefill", rebuild the 4-bit weights as bf16 inside the grouped GEMM and
+   credit that with a large prefill speed-up over expanding them first):
+   writes the bf16 weights w = bf16(scale * q + bias) of every expert with
+   routing->counts[e] > 0 and of the shared expert to device memory, for
+   lily_moe_forward_bf16. packed: the layer's packed stacks, as for
+   lily_moe_forward; bf16: six caller-owned bf16 [n][N][K] row-major stacks
+   with the same roles (gate and up [E][F][H], down [E][H][F], shared ones
+   n = 1); entries of experts with no rows are left untouched. The values
+   are the ones the fused GEMMs multiply with, bit for bit. Errors as
+   lily_moe_forward. */
+int lily_moe_dequant(const lily_moe_dims* dims, const lily_moe_weights* packed,
+                     const lily_moe_routing* routing, const lily_moe_weights* bf16,
+                     void* stream);
+
+/* The forward of lily_moe_forward reading the bf16 stacks that
+   lily_moe_dequant wrote instead of the packed int4 ones: the same grouped
+   GEMM with its weight tiles loaded as bf16 (nothing dequantised), the same
+   SwiGLU and combine. The output is bit-identical to lily_moe_forward's for
+   the same routing. tile_m must be 32 or 64. Errors as lily_moe_forward,
+   plus LILY_ERR_UNSUPPORTED for tile_m 128. */
+int lily_moe_forward_bf16(const lily_moe_dims* dims, const lily_moe_weights* bf16,
+                          const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Route and forward of one MoE layer for a few tokens (T <= 4, decode) in
    one launch: the routing of lily_moe_route (same ids and weights) and the
    output of lily_moe_forward up to rounding: the weights enter as the exact

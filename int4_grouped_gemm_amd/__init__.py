@@ -25,7 +25,7 @@ LILY_ERR_HIP = -4
 
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
            "lily_w4_pack", "lily_moe_router", "lily_moe_route", "lily_moe_route_host",
-           "lily_moe_forward", "lily_moe_gate_up",
+           "lily_moe_forward", "lily_moe_dequant", "lily_moe_forward_bf16", "lily_moe_gate_up",
            "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_residual_norm",
            "lily_last_error")
 LILY_SCHED_INTS = 1056
@@ -98,6 +98,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_moe_forward.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
                                      P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.lily_moe_dequant.restype = ctypes.c_int
+    lib.lily_moe_dequant.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), P(LilyMoeRouting),
+                                     P(LilyMoeWeights), ctypes.c_void_p]
+    lib.lily_moe_forward_bf16.restype = ctypes.c_int
+    lib.lily_moe_forward_bf16.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
+                                          P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
     lib.lily_moe_gate_up.restype = ctypes.c_int
     lib.lily_moe_gate_up.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
                                      P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_size_t,
@@ -268,6 +275,37 @@ def lily_moe_forward(d: LilyMoeDims, weights: Weights, x, routing: Routing, out,
 
 def _ws_bytes(workspace) -> int:
     return workspace.numel() * workspace.element_size()
+
+
+def lily_moe_dequant(d: LilyMoeDims, packed: Weights, routing: Routing, bf16: Weights,
+                     stream=None) -> None:
+    """Unfused twin, step 1: bf16 weights of the experts with rows (and the
+    shared expert) into the stacks of ``bf16`` (see alloc_bf16_weights)."""
+    lib = load()
+    rc = lib.lily_moe_dequant(ctypes.byref(d), ctypes.byref(packed.c()), ctypes.byref(routing.c()),
+                              ctypes.byref(bf16.c()), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_forward_bf16(d: LilyMoeDims, bf16: Weights, x, routing: Routing, out, workspace,
+                          workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """Unfused twin, step 2: the forward reading the bf16 stacks."""
+    lib = load()
+    nbytes = _ws_bytes(workspace) if workspace_bytes is None else workspace_bytes
+    rc = lib.lily_moe_forward_bf16(ctypes.byref(d), ctypes.byref(bf16.c()), _ptr(x),
+                                   ctypes.byref(routing.c()), _ptr(out), _ptr(workspace), nbytes,
+                                   _stream(stream))
+    _check(rc, lib)
+
+
+def alloc_bf16_weights(d: LilyMoeDims, device="cuda") -> Weights:
+    """Caller-owned bf16 [n][N][K] stacks for lily_moe_dequant (bf16 bits as
+    int16): gate and up [E][F][H], down [E][H][F], the shared ones n = 1."""
+    E, H, F = d.E, d.H, d.F
+    e16 = dict(dtype=torch.int16, device=device)
+    return Weights(gate=torch.empty((E, F, H), **e16), up=torch.empty((E, F, H), **e16),
+                   down=torch.empty((E, H, F), **e16), sh_gate=torch.empty((1, F, H), **e16),
+                   sh_up=torch.empty((1, F, H), **e16), sh_down=torch.empty((1, H, F), **e16))
 
 
 def lily_moe_gate_up(d: LilyMoeDims, weights: Weights, x, routing: Routing, workspace,

@@ -29,9 +29,11 @@ int launch_route_host(const lily_moe_dims& d, const float* logits, const lily_mo
                       hipStream_t stream);
 int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
                    const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
-                   hipStream_t stream);
+                   hipStream_t stream, bool w4);
 int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_moe_routing& r,
-                int max_blocks, const ForwardWorkspace& ws, hipStream_t stream);
+                int max_blocks, const ForwardWorkspace& ws, hipStream_t stream, bool w4);
+int launch_dequant(const void* packed, int n, int N, int K, const int32_t* counts, void* out,
+                   hipStream_t stream);
 int launch_combine(const lily_moe_dims& d, const ForwardWorkspace& ws, const lily_moe_routing& r,
                    uint16_t* out, hipStream_t stream);
 size_t forward_workspace_bytes(const lily_moe_dims& d, int max_blocks);
@@ -229,8 +231,51 @@ int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
     const ForwardWorkspace ws = forward_workspace_split(*dims, workspace);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int mb = max_blocks_of(*dims);
-    if ((rc = launch_gate_up(*dims, *weights, x, *routing, mb, ws, s))) return rc;
-    if ((rc = launch_down(*dims, *weights, *routing, mb, ws, s))) return rc;
+    if ((rc = launch_gate_up(*dims, *weights, x, *routing, mb, ws, s, true))) return rc;
+    if ((rc = launch_down(*dims, *weights, *routing, mb, ws, s, true))) return rc;
+    return launch_combine(*dims, ws, *routing, out, s);
+}
+
+int lily_moe_dequant(const lily_moe_dims* dims, const lily_moe_weights* packed,
+                     const lily_moe_routing* routing, const lily_moe_weights* bf16, void* stream) {
+    int rc = check_forward_args(dims, packed, routing);
+    if (rc) return rc;
+    if (!bf16) return set_error(LILY_ERR_INVALID_ARG, "bf16 is NULL");
+    REQUIRE_PTR(bf16->gate);
+    REQUIRE_PTR(bf16->up);
+    REQUIRE_PTR(bf16->down);
+    REQUIRE_PTR(bf16->sh_gate);
+    REQUIRE_PTR(bf16->sh_up);
+    REQUIRE_PTR(bf16->sh_down);
+    // The weight struct's pointers are const; here they name the outputs.
+    const lily_moe_dims& d = *dims;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int32_t* c = routing->counts;
+    if ((rc = launch_dequant(packed->gate, d.E, d.F, d.H, c, const_cast<void*>(bf16->gate), s)) ||
+        (rc = launch_dequant(packed->up, d.E, d.F, d.H, c, const_cast<void*>(bf16->up), s)) ||
+        (rc = launch_dequant(packed->down, d.E, d.H, d.F, c, const_cast<void*>(bf16->down), s)) ||
+        (rc = launch_dequant(packed->sh_gate, 1, d.F, d.H, nullptr, const_cast<void*>(bf16->sh_gate), s)) ||
+        (rc = launch_dequant(packed->sh_up, 1, d.F, d.H, nullptr, const_cast<void*>(bf16->sh_up), s)))
+        return rc;
+    return launch_dequant(packed->sh_down, 1, d.H, d.F, nullptr, const_cast<void*>(bf16->sh_down), s);
+}
+
+int lily_moe_forward_bf16(const lily_moe_dims* dims, const lily_moe_weights* bf16,
+                          const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_forward_args(dims, bf16, routing);
+    if (rc) return rc;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(out);
+    if (dims->tile_m != 32 && dims->tile_m != 64)
+        return set_error(LILY_ERR_UNSUPPORTED, "tile_m = %d; the bf16 GEMMs take 32 or 64",
+                         dims->tile_m);
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    const ForwardWorkspace ws = forward_workspace_split(*dims, workspace);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int mb = max_blocks_of(*dims);
+    if ((rc = launch_gate_up(*dims, *bf16, x, *routing, mb, ws, s, false))) return rc;
+    if ((rc = launch_down(*dims, *bf16, *routing, mb, ws, s, false))) return rc;
     return launch_combine(*dims, ws, *routing, out, s);
 }
 
@@ -243,7 +288,7 @@ int lily_moe_gate_up(const lily_moe_dims* dims, const lily_moe_weights* weights,
     if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
     return launch_gate_up(*dims, *weights, x, *routing, max_blocks_of(*dims),
                           forward_workspace_split(*dims, workspace),
-                          reinterpret_cast<hipStream_t>(stream));
+                          reinterpret_cast<hipStream_t>(stream), true);
 }
 
 int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
@@ -254,7 +299,7 @@ int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
     if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
     return launch_down(*dims, *weights, *routing, max_blocks_of(*dims),
                        forward_workspace_split(*dims, workspace),
-                       reinterpret_cast<hipStream_t>(stream));
+                       reinterpret_cast<hipStream_t>(stream), true);
 }
 
 int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,

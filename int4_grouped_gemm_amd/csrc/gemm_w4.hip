@@ -105,17 +105,23 @@ struct Occ {
 // rows][16 B]), the scales and biases (SB: [256] bf16 then [256] bf16) and
 // the A tile ([BM rows][64 bf16]). All stage bases stay below 64 KB so they
 // fit the immediate offset of ds_read.
-template <int BM>
+//
+// W4 = false is the unfused twin: the weights arrive as bf16 rows ([256
+// rows][64 bf16], 16-byte chunks swizzled like A) and nothing is
+// dequantised. Its stages are four times larger, so it keeps two stages
+// and BM <= 64 (two workgroups per compute unit).
+template <int BM, bool W4 = true>
 struct Lds {
-    static constexpr int NS = Occ<BM>::NS;
-    static constexpr int Q = 256 * 32;
-    static constexpr int SB = 256 * 2 * 2;
+    static constexpr int NS = W4 ? Occ<BM>::NS : 2;
+    static constexpr int Q = W4 ? 256 * 32 : 256 * 128;
+    static constexpr int SB = W4 ? 256 * 2 * 2 : 0;
     static constexpr int A = BM * 128;
-    static constexpr int Q_OFF = 0;
+    static constexpr int Q_OFF = W4 ? 0 : NS * A;
     static constexpr int SB_OFF = Q_OFF + NS * Q;
-    static constexpr int A_OFF = SB_OFF + NS * SB;
-    static constexpr int TOTAL = A_OFF + NS * A;
-    static_assert(A_OFF + (NS - 1) * A < 65536, "stage bases must fit ds_read offsets");
+    static constexpr int A_OFF = W4 ? SB_OFF + NS * SB : 0;
+    static constexpr int TOTAL = NS * (A + Q + SB);
+    static_assert(A_OFF + (NS - 1) * A < 65536 && Q_OFF + (NS - 1) * Q < 65536,
+                  "stage bases must fit ds_read offsets");
 };
 
 // s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
@@ -170,7 +176,7 @@ __device__ __forceinline__ int grab(int32_t* ctr, int* s_slot, int& toggle) {
 // One work item (a (block, n-tile) tile) and the load plan of one
 // wavefront for it: the A row offsets of its DMA loads and the packed block
 // of its weight slab at k-step 0 (+ kt * kPackBlock).
-template <int MI>
+template <int MI, bool W4 = true>
 struct Item {
     bool valid;
     bool prefetched;         // its first NS - 1 stages are already in flight
@@ -179,22 +185,31 @@ struct Item {
     int chunk, tile;         // K chunk of the item (split K) and its tile's counter index
     const char* a_base;      // A rows: + kt * 128
     uint32_t a_off[MI];      // row byte offset + swizzled chunk
-    const char* w_base;
+    const char* w_base;      // packed weights (W4), or the wavefront's bf16 matrix: + kt * 128
+    uint32_t b_off[W4 ? 1 : 8];  // bf16 weights: row byte offset + swizzled chunk
 };
 
 // DMA of one k-step stage of an item by one wavefront: its n_a A loads
 // (8 rows each, n_a <= MI), then half wh of weight slab wb (rows 0-63 and
 // 64-127, 1 KB each) and the slab's 128 scales (wh = 0) or biases (wh = 1).
 // N_DMA = n_a + 3 loads in all.
-template <int BM>
-__device__ __forceinline__ void issue_stage(const Item<BM / 32>& it, int n_a, int kt, int buf,
+// The unfused twin (W4 = false) loads the wavefront's 64 bf16 weight rows
+// instead: 8 loads of 8 rows. N_DMA = n_a + 8.
+template <int BM, bool W4 = true>
+__device__ __forceinline__ void issue_stage(const Item<BM / 32, W4>& it, int n_a, int kt, int buf,
                                             uint32_t smem, uint32_t wave, int lane) {
-    using Ld = Lds<BM>;
+    using Ld = Lds<BM, W4>;
 #pragma unroll
     for (int j = 0; j < BM / 32; ++j)
         if (j < n_a)
             dma16(it.a_base + kt * 128, it.a_off[j],
                   smem + Ld::A_OFF + buf * Ld::A + (32 * j + 8 * wave) * 128);
+    if constexpr (!W4) {
+        const uint32_t b_lds = smem + Ld::Q_OFF + buf * Ld::Q + 64u * wave * 128u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16(it.w_base + kt * 128, it.b_off[j], b_lds + j * 8 * 128);
+        return;
+    }
     const uint32_t wh = wave & 1u, wb = wave >> 1;
     const uint32_t q_off = (wh * 128u + (uint32_t)lane) * 16u;
     const uint32_t sb_off = (uint32_t)kPackQ + wh * 256u + (uint32_t)lane * 4u;
@@ -209,15 +224,15 @@ __device__ __forceinline__ void issue_stage(const Item<BM / 32>& it, int n_a, in
 // Loads, multiplies and stores one tile. `prep_next` runs between the
 // k-loop and the stores: it takes and resolves the workgroup's next item, so
 // that the latency of its metadata loads overlaps the stores.
-template <int BM, bool GATED, int MIA, typename PrepNext>
+template <int BM, bool GATED, int MIA, bool W4, typename PrepNext>
 __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
-                                          const Item<BM / 32>& lp, uint32_t wave, int* s_flag,
+                                          const Item<BM / 32, W4>& lp, uint32_t wave, int* s_flag,
                                           PrepNext&& prep_next) {
-    using Ld = Lds<BM>;
+    using Ld = Lds<BM, W4>;
     constexpr int NS = Ld::NS;
     constexpr int NI = 2;
     constexpr int N_A = MIA;  // A loads per wavefront per k-step (8 rows each)
-    constexpr int N_DMA = N_A + 3;
+    constexpr int N_DMA = N_A + (W4 ? 3 : 8);
     static_assert(NS == 2 || NS == 3, "stage count");
     const uint32_t smem = (uint32_t)(size_t)smem_p;  // LDS byte address
     const int lane = threadIdx.x % kWave;
@@ -231,7 +246,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         col0[g] = GATED ? lp.n0 + 32 * (int)wave : lp.n0 + 64 * (int)wave + 32 * g;
     }
 
-    auto issue = [&](int kt, int buf) { issue_stage<BM>(lp, MIA, kt, buf, smem, wave, lane); };
+    auto issue = [&](int kt, int buf) { issue_stage<BM, W4>(lp, MIA, kt, buf, smem, wave, lane); };
 
     f32x16 acc[MIA][NI];
 #pragma unroll
@@ -249,11 +264,13 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         const int row = lane % 32;
         a_rd[s] = row * 128 + swz(row, 4 * h + s) * 16;
     }
-    uint32_t q_rd[NI], sb_rd[NI];
+    uint32_t q_rd[NI], sb_rd[NI], b_rd[NI][4];
 #pragma unroll
     for (int g = 0; g < NI; ++g) {
         q_rd[g] = (h * 256 + brow[g]) * 16;
         sb_rd[g] = brow[g] * 2;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b_rd[g][s] = brow[g] * 128 + swz(brow[g], 4 * h + s) * 16;
     }
 
     // One k-step on stage buffer `buf` (a compile-time constant after the
@@ -267,6 +284,26 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         const char* Ab = smem_p + Ld::A_OFF + buf * Ld::A;
         const char* Qb = smem_p + Ld::Q_OFF + buf * Ld::Q;
         const char* Sb = smem_p + Ld::SB_OFF + buf * Ld::SB;
+        if constexpr (!W4) {
+            // Unfused twin: the bf16 weight fragments are read from LDS like
+            // the A fragments; nothing is dequantised.
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 af[MIA], bfr[NI];
+#pragma unroll
+                for (int i = 0; i < MIA; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8*>(Ab + i * 4096 + a_rd[s]);
+#pragma unroll
+                for (int g = 0; g < NI; ++g) bfr[g] = *reinterpret_cast<const bf16x8*>(Qb + b_rd[g][s]);
+#pragma unroll
+                for (int i = 0; i < MIA; ++i)
+#pragma unroll
+                    for (int g = 0; g < NI; ++g)
+                        acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[g], acc[i][g], 0, 0, 0);
+            }
+            wait_lgkmcnt0();
+            return;
+        }
         // The weights' LDS reads are issued first and each sub-step's A
         // fragments one sub-step ahead; the MFMAs of sub-step s run while
         // the weights of sub-step s + 1 are dequantised.
@@ -428,11 +465,12 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
     }
 }
 
-template <int BM, bool GATED>
-__global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_gemm(GemmArgs args) {
+template <int BM, bool GATED, bool W4 = true>
+__global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2)
+    moe_w4_gemm(GemmArgs args) {
     constexpr int BN = GemmShape<GATED>::BN;
     constexpr int MI = BM / 32;
-    __shared__ __attribute__((aligned(16))) char smem[Lds<BM>::TOTAL];
+    __shared__ __attribute__((aligned(16))) char smem[Lds<BM, W4>::TOTAL];
     __shared__ int s_slot[3];  // two alternating queue slots, the split-K arrival count
 
     const int tid = threadIdx.x;
@@ -461,7 +499,7 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
     // Takes the next item of queue cq (one atomic) and resolves its rows,
     // expert and load plan (one load of block_info); it.valid = false if the
     // queue is empty.
-    auto take = [&](Item<MI>& it) {
+    auto take = [&](Item<MI, W4>& it) {
         it.valid = false;
         const int c = grab(args.sched + cq, s_slot, toggle);
         if (c >= items_of(cq)) return;
@@ -508,8 +546,22 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
             // 2 nt + wb.
             const int wb = (int)(wave >> 1);
             const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
-            const int slab = GATED ? nt : 2 * nt + wb;
-            it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes + (size_t)kt0 * kPackBlock;
+            if constexpr (W4) {
+                const int slab = GATED ? nt : 2 * nt + wb;
+                it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes + (size_t)kt0 * kPackBlock;
+            } else {
+                // bf16 [n][N][K] stacks: the wavefront loads the workgroup's
+                // weight rows 64 w .. 64 w + 63 (LDS rows, swizzled like A):
+                // gate/up -> row n0 + (64 w + i) % 128 of the gate or up
+                // matrix; down -> row n0 + 64 w + i.
+                it.w_base = stack + (size_t)e * args.N * args.K * 2 + (size_t)kt0 * 128;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int lrow = 64 * (int)wave + 8 * j + lane / 8;
+                    const int n = it.n0 + (GATED ? lrow % 128 : lrow);
+                    it.b_off[j] = (uint32_t)n * (uint32_t)(args.K * 2) + (uint32_t)(swz(lrow, lane % 8) * 16);
+                }
+            }
             it.valid = true;
             return;
         }
@@ -517,10 +569,10 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
     // Every decision follows a value that grab() sent through LDS, so all
     // wavefronts take the same path and meet at the same barriers.
     const uint32_t smem_addr = (uint32_t)(size_t)smem;
-    Item<MI> cur;
+    Item<MI, W4> cur;
     take(cur);
     while (cur.valid) {
-        Item<MI> nxt;
+        Item<MI, W4> nxt;
         // After the k-loop (every wavefront is done with the LDS stages):
         // take the next item and start its first stages, so that their
         // latency overlaps this tile's stores.
@@ -528,18 +580,18 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD) moe_w4_
             take(nxt);
             if (nxt.valid) {
 #pragma unroll
-                for (int u = 0; u < Lds<BM>::NS - 1; ++u)
-                    if (u < args.K / 64 / args.kc) issue_stage<BM>(nxt, nxt.mia, u, u, smem_addr, wave, lane);
+                for (int u = 0; u < Lds<BM, W4>::NS - 1; ++u)
+                    if (u < args.K / 64 / args.kc) issue_stage<BM, W4>(nxt, nxt.mia, u, u, smem_addr, wave, lane);
                 nxt.prefetched = true;
             }
         };
         // Only the 32-row sub-tiles that hold rows of the block are loaded
         // and multiplied.
         const int mia = cur.mia;
-        if (mia >= MI) gemm_main<BM, GATED, MI>(args, smem, cur, wave, s_slot + 2, prep);
-        else if (mia == 1) gemm_main<BM, GATED, 1>(args, smem, cur, wave, s_slot + 2, prep);
-        else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1)>(args, smem, cur, wave, s_slot + 2, prep);
-        else gemm_main<BM, GATED, (MI > 3 ? 3 : 1)>(args, smem, cur, wave, s_slot + 2, prep);
+        if (mia >= MI) gemm_main<BM, GATED, MI, W4>(args, smem, cur, wave, s_slot + 2, prep);
+        else if (mia == 1) gemm_main<BM, GATED, 1, W4>(args, smem, cur, wave, s_slot + 2, prep);
+        else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1), W4>(args, smem, cur, wave, s_slot + 2, prep);
+        else gemm_main<BM, GATED, (MI > 3 ? 3 : 1), W4>(args, smem, cur, wave, s_slot + 2, prep);
         cur = nxt;
     }
 
@@ -572,6 +624,51 @@ __global__ void __launch_bounds__(256) pack_w4_kernel(const uint8_t* __restrict_
     *reinterpret_cast<u32x4*>(blk + (kPackRows + r) * 16) = src[1];
     *reinterpret_cast<uint16_t*>(blk + kPackQ + r * 2) = scale[idx];
     *reinterpret_cast<uint16_t*>(blk + kPackQ + 2 * kPackRows + r * 2) = bias[idx];
+}
+
+// Unfused twin: the packed int4 stack -> bf16 [n][N][K] in device memory,
+// with the same dequantisation as the fused GEMMs (so the GEMMs that read
+// it compute bit for bit what the fused ones do). One thread per (expert,
+// row, group of 64); experts with counts[e] == 0 are skipped (counts may be
+// NULL: all experts).
+__global__ void __launch_bounds__(256) dequant_w4_kernel(const char* __restrict__ packed, int n,
+                                                         int N, int K,
+                                                         const int32_t* __restrict__ counts,
+                                                         uint16_t* __restrict__ out) {
+    const int groups = K / 64;
+    const long total = (long)n * N * groups;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const long er = idx / groups;  // e * N + row
+    const int g = (int)(idx - er * groups);
+    const int row = (int)(er % N);
+    const long e = er / N;
+    if (counts && counts[e] == 0) return;
+    const char* blk = packed + ((e * (N / kPackRows) + row / kPackRows) * groups + g) * (long)kPackBlock;
+    const int r = row % kPackRows;
+    const float s512 = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + kPackQ + r * 2)) * 512.0f;
+    const float b = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + kPackQ + 2 * kPackRows + r * 2));
+    u32x4* dst = reinterpret_cast<u32x4*>(out + er * K + g * 64);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(blk + (half * kPackRows + r) * 16);
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            uint32_t o[4];
+            dequant8(q[wd], s512, b, o);
+            dst[half * 4 + wd] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
+int launch_dequant(const void* packed, int n, int N, int K, const int32_t* counts, void* out,
+                   hipStream_t stream) {
+    const long total = (long)n * N * (K / 64);
+    const long grid = (total + 255) / 256;
+    hipLaunchKernelGGL(dequant_w4_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const char*>(packed), n, N, K, counts,
+                       static_cast<uint16_t*>(out));
+    return check_launch("dequant_w4");
 }
 
 // out[t] = bf16(y[P + t] + sum_j w[t, j] * y[pair_rows[t * topk + j]]), fp32,
@@ -667,7 +764,7 @@ static GemmArgs routing_args(const lily_moe_dims& d, const lily_moe_routing& r) 
 // Persistent grid: the workgroups that fit on the device at once (from the
 // kernel's own occupancy), fewer if the largest possible block map has
 // fewer items (tiles times K chunks), a multiple of the queue count.
-template <int BM, bool GATED>
+template <int BM, bool GATED, bool W4>
 static int gemm_grid(GemmArgs& g, int max_blocks) {
     constexpr int kMaxDevices = 64;
     static int resident[kMaxDevices];
@@ -678,7 +775,7 @@ static int gemm_grid(GemmArgs& g, int max_blocks) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_w4_gemm<BM, GATED>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_w4_gemm<BM, GATED, W4>,
                                                          kGemmThreads, 0) != hipSuccess)
             per_cu = 0;
         slots = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
@@ -690,24 +787,25 @@ static int gemm_grid(GemmArgs& g, int max_blocks) {
     return (int)((grid + kXcds - 1) / kXcds * kXcds);
 }
 
-template <int BM>
+template <int BM, bool W4>
 static int launch_gate_up_bm(GemmArgs g, int max_blocks, hipStream_t stream) {
-    const dim3 grid(gemm_grid<BM, true>(g, max_blocks));
-    hipLaunchKernelGGL((moe_w4_gemm<BM, true>), grid, dim3(kGemmThreads), 0, stream, g);
+    const dim3 grid(gemm_grid<BM, true, W4>(g, max_blocks));
+    hipLaunchKernelGGL((moe_w4_gemm<BM, true, W4>), grid, dim3(kGemmThreads), 0, stream, g);
     return check_launch("gate_up_gemm");
 }
 
-template <int BM>
+template <int BM, bool W4>
 static int launch_down_bm(GemmArgs g, int max_blocks, hipStream_t stream) {
-    const dim3 grid(gemm_grid<BM, false>(g, max_blocks));
-    hipLaunchKernelGGL((moe_w4_gemm<BM, false>), grid, dim3(kGemmThreads), 0, stream, g);
+    const dim3 grid(gemm_grid<BM, false, W4>(g, max_blocks));
+    hipLaunchKernelGGL((moe_w4_gemm<BM, false, W4>), grid, dim3(kGemmThreads), 0, stream, g);
     return check_launch("down_gemm");
 }
 
 // G1 + G2 (and the shared expert's rows): h = bf16(silu(x Wg^T) * (x Wu^T)).
+// w4 = false: the unfused twin, whose weights are bf16 [n][N][K] stacks.
 int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
                    const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
-                   hipStream_t stream) {
+                   hipStream_t stream, bool w4) {
     GemmArgs g = routing_args(d, r);
     g.a = x;
     g.sorted_pairs = r.sorted_pairs;
@@ -722,17 +820,22 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
     g.kc = split_k(d, max_blocks, true);
     g.part = ws.part;
     g.tile_ctr = r.sched + kQueueInts;
+    if (!w4) {
+        if (d.tile_m == 32) return launch_gate_up_bm<32, false>(g, max_blocks, stream);
+        if (d.tile_m == 64) return launch_gate_up_bm<64, false>(g, max_blocks, stream);
+        return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d; the bf16 GEMMs take 32 or 64", d.tile_m);
+    }
     switch (d.tile_m) {
-        case 32: return launch_gate_up_bm<32>(g, max_blocks, stream);
-        case 64: return launch_gate_up_bm<64>(g, max_blocks, stream);
-        case 128: return launch_gate_up_bm<128>(g, max_blocks, stream);
+        case 32: return launch_gate_up_bm<32, true>(g, max_blocks, stream);
+        case 64: return launch_gate_up_bm<64, true>(g, max_blocks, stream);
+        case 128: return launch_gate_up_bm<128, true>(g, max_blocks, stream);
     }
     return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
 }
 
 // G3 (and the shared expert's rows): y = h Wd^T in fp32.
 int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_moe_routing& r,
-                int max_blocks, const ForwardWorkspace& ws, hipStream_t stream) {
+                int max_blocks, const ForwardWorkspace& ws, hipStream_t stream, bool w4) {
     GemmArgs g = routing_args(d, r);
     g.a = ws.h;
     g.w[0] = g.w[1] = static_cast<const char*>(w.down);
@@ -744,10 +847,15 @@ int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_mo
     g.kc = split_k(d, max_blocks, false);
     g.part = ws.part;
     g.tile_ctr = r.sched + kQueueInts + kTileCounters;
+    if (!w4) {
+        if (d.tile_m == 32) return launch_down_bm<32, false>(g, max_blocks, stream);
+        if (d.tile_m == 64) return launch_down_bm<64, false>(g, max_blocks, stream);
+        return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d; the bf16 GEMMs take 32 or 64", d.tile_m);
+    }
     switch (d.tile_m) {
-        case 32: return launch_down_bm<32>(g, max_blocks, stream);
-        case 64: return launch_down_bm<64>(g, max_blocks, stream);
-        case 128: return launch_down_bm<128>(g, max_blocks, stream);
+        case 32: return launch_down_bm<32, true>(g, max_blocks, stream);
+        case 64: return launch_down_bm<64, true>(g, max_blocks, stream);
+        case 128: return launch_down_bm<128, true>(g, max_blocks, stream);
     }
     return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
 }

@@ -109,6 +109,19 @@ def test_route_rejects_pointers(lib):
     assert lib.lily_moe_route(None, FAKE, ctypes.byref(routing()), None) == L.LILY_ERR_INVALID_ARG
 
 
+def test_unfused_twin_rejects(lib):
+    d = good_dims(tile_m=128)
+    rc = lib.lily_moe_forward_bf16(ctypes.byref(d), ctypes.byref(weights()), FAKE,
+                                   ctypes.byref(routing()), FAKE, FAKE, 1 << 40, None)
+    assert rc == L.LILY_ERR_UNSUPPORTED and "tile_m" in lib.lily_last_error().decode()
+    rc = lib.lily_moe_dequant(ctypes.byref(good_dims()), ctypes.byref(weights()),
+                              ctypes.byref(routing()), None, None)
+    assert rc == L.LILY_ERR_INVALID_ARG and "bf16" in lib.lily_last_error().decode()
+    rc = lib.lily_moe_dequant(ctypes.byref(good_dims()), ctypes.byref(weights()),
+                              ctypes.byref(routing()), ctypes.byref(weights(down=None)), None)
+    assert rc == L.LILY_ERR_INVALID_ARG and "down" in lib.lily_last_error().decode()
+
+
 def test_route_host_rejects(lib):
     """The host-synchronised twin validates like lily_moe_route, before any
     device work."""

@@ -126,6 +126,51 @@ def test_route_host_twin_forward():
     assert np.array_equal(a, b), "forward after the host route differs"
 
 
+@pytest.mark.parametrize("name,tile_m", [("tiny", 32), ("tiny", 64), ("prefill512", 64),
+                                         ("prefill2048_zipf", 64), ("prefill2048_zipf", 32)])
+def test_unfused_twin(name, tile_m):
+    """lily_moe_dequant + lily_moe_forward_bf16 (the unfused twin): the bf16
+    weights it writes equal the oracle's dequantisation bit for bit; experts
+    without rows are left untouched; and its output is bit-identical to the
+    fused lily_moe_forward (same weights, same products in the same order)."""
+    cfg = S.CONFIGS[name]
+    _flush(f"unfused twin {name} tile_m={tile_m}")
+    lw = S.layer_weights(cfg, 0)
+    x = S.activations(cfg, 0)
+    lg = S.router_logits(cfg, 0, 0)
+    d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, tile_m)
+    w = L.weights_from_host(lw)
+    xd = G.to_dev_bits(x)
+    r = G.route_gpu(d, lg)
+    fused = G.from_dev_bits(G.forward_gpu(d, w, xd, r))
+    bw = L.alloc_bf16_weights(d)
+    for name_ in L.WEIGHT_FIELDS:
+        getattr(bw, name_).fill_(0x7FC1)  # a NaN pattern: untouched entries stay so
+    L.lily_moe_dequant(d, w, r, bw)
+    torch.cuda.synchronize()
+    counts = r.counts.cpu().numpy()
+    used = np.flatnonzero(counts)
+    unused = np.flatnonzero(counts == 0)
+    for t, (routed, shared) in enumerate([(bw.gate, bw.sh_gate), (bw.up, bw.sh_up),
+                                          (bw.down, bw.sh_down)]):
+        get = oracle.getter_from_layer(lw)
+        for e in ([int(used[0]), int(used[-1])] if len(used) else []):
+            want = oracle.dequant(*get(t, e))
+            assert np.array_equal(routed[e].cpu().numpy().view(np.uint16), want), (t, e)
+        want = oracle.dequant(*get(t, cfg.E))
+        assert np.array_equal(shared[0].cpu().numpy().view(np.uint16), want), (t, "shared")
+        if len(unused):
+            assert np.all(routed[int(unused[0])].cpu().numpy() == 0x7FC1), (t, "unused touched")
+    ws = L.alloc_workspace(d)
+    ws.fill_(0xFF)
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device="cuda")
+    L.lily_moe_forward_bf16(d, bw, xd, r, out, ws)
+    torch.cuda.synchronize()
+    got = G.from_dev_bits(out)
+    assert np.array_equal(got, fused), "unfused twin differs from the fused forward"
+    assert not np.any(r.sched.cpu().numpy()), "GEMMs must leave their queue counters zero"
+
+
 # ------------------------------------------------------------------- forward
 
 def _layer_case(cfg, tile_m, tokens=None, layer=0, seed=0):
