@@ -31,6 +31,7 @@ namespace lily {
 constexpr int kDecThreads = 256;
 constexpr int kDecodeMaxT = 4;       // lily_moe_decode serves T <= this
 constexpr int kDecMaxGrid = 512;     // workgroups: at most one per compute unit and this
+constexpr int kDecXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round robin over them
 constexpr int kDecASlices = 8;       // phase A slices per lane and weight matrix loaded at once
 constexpr int kDecBRounds = 6;       // phase B rounds per wavefront loaded at once
 constexpr int kDecLdsWords = 8192;   // LDS: x rows (phase A) or h rows (phase B), bf16 pairs
@@ -196,6 +197,10 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     const int wave = tid / kWave;
     const int G = gridDim.x;
     const int wg = blockIdx.x;
+    // Units are dealt by this index, which numbers the workgroups XCD by
+    // XCD (workgroup w runs on XCD w % 8): consecutive units, which share
+    // the scale and bias lines of their packed blocks, meet in one L2.
+    const int vw = G % kDecXcds == 0 ? (wg % kDecXcds) * (G / kDecXcds) + wg / kDecXcds : wg;
     const int k = a.k;
     const int R = a.T * (k + 1);
     const int H = a.H, F = a.F;
@@ -237,7 +242,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int pieces_per_tok = H / kDecPiece;
     const int UB = a.T * pieces_per_tok;
-    const int ub0 = range_begin(wg, UB, G), ub1 = range_begin(wg + 1, UB, G);
+    const int ub0 = range_begin(vw, UB, G), ub1 = range_begin(vw + 1, UB, G);
     const int nq = nkgF / 4;
     const int NRB = (k + 1) * nq;
     const int b_gl = lane / 16, b_half = (lane / 8) % 2, b_row = lane % kDecPiece;
@@ -271,7 +276,8 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
 
     // Phase A: unit u = (row r, features f0 .. f0 + 7): the 8 gate rows and
     // the 8 up rows of those features over all of K, one wavefront per unit;
-    // units are dealt to workgroup u % G, then to its wavefronts in turn.
+    // units are dealt to the workgroup with vw = u % G, then to its
+    // wavefronts in turn.
     // Lane l covers feature f0 + l % 8 and the 32-weight slices c = l / 8 +
     // 8 i of its rows (group c / 2, half c % 2): each load instruction reads
     // whole 128-byte lines (8 rows x 16 bytes of one block half). The sums
@@ -282,7 +288,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     const int spr8 = H / 256;  // slices per lane per weight row
     const int l8 = lane % 8, lc = lane / 8;
     bool b_loaded = false;
-    for (int u = wg + G * wv; u < UA; u += 4 * G) {
+    for (int u = vw + G * wv; u < UA; u += 4 * G) {
         const int r = u / (F / 8), f0 = (u - r * (F / 8)) * 8;
         const int t = r / (k + 1), j = r - t * (k + 1);
         const bool sh = (j == k);
