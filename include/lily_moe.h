@@ -128,12 +128,16 @@ typedef struct {
                               learns a block's extent with one load;
    sched int32 [LILY_SCHED_INTS]
                               work-queue and split-K tile counters of the
-                              grouped GEMMs. Zero them once after
-                              allocating; lily_moe_route clears them and
-                              every GEMM launch leaves them zero when it
-                              completes. Launches that share a routing
-                              buffer must be ordered on one stream. */
-#define LILY_SCHED_INTS 1056
+                              grouped GEMMs (the first 1056 ints), then the
+                              route's per-span expert histograms (64 rows of
+                              512 counts and an arrival counter). Zero the
+                              whole array once after allocating;
+                              lily_moe_route clears the counters and leaves
+                              the histograms zero, and every GEMM launch
+                              leaves its counters zero when it completes.
+                              Launches that share a routing buffer must be
+                              ordered on one stream. */
+#define LILY_SCHED_INTS (1056 + 64 * 512 + 1)
 typedef struct {
     int32_t* topk_ids;
     float* topk_w;

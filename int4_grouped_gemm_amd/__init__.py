@@ -28,7 +28,7 @@ EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_by
            "lily_moe_forward", "lily_moe_dequant", "lily_moe_forward_bf16", "lily_moe_gate_up",
            "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_residual_norm",
            "lily_last_error")
-LILY_SCHED_INTS = 1056
+LILY_SCHED_INTS = 1056 + 64 * 512 + 1
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
 

@@ -13,10 +13,16 @@ constexpr int kGroup = 64;     // weights per (scale, bias) group
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 64;
 // The routing's sched array: 16 queue/finish counters per GEMM (gate/up,
-// down), then the split-K tile counters of each GEMM.
+// down), then the split-K tile counters of each GEMM (kCounterInts in
+// all), then the route's per-part expert histograms: kMaxParts rows of
+// kMaxExperts counts and one arrival counter.
 constexpr int kSchedInts = LILY_SCHED_INTS;
 constexpr int kQueueInts = 32;
-constexpr int kTileCounters = (kSchedInts - kQueueInts) / 2;
+constexpr int kCounterInts = 1056;
+constexpr int kTileCounters = (kCounterInts - kQueueInts) / 2;
+constexpr int kMaxParts = 64;
+constexpr int kPartBase = kCounterInts;
+static_assert(kPartBase + kMaxParts * kMaxExperts + 1 == kSchedInts, "sched layout");
 // sched[28], sched[29]: the fused decode kernel's device-wide barrier
 // (arrivals, exits); sched[30]: set if one of its barrier waits gave up.
 constexpr int kDecodeBarrier = 28;

@@ -46,10 +46,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // order-preserving keys; a taken expert's key becomes 0, below every real
 // key. Each round takes the wavefront maximum and, among the experts holding
 // it, the lowest index (ballots in expert order).
+// hist, when not null, counts the chosen experts (integer atomics: the
+// totals do not depend on their order).
 template <int NPER>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
                                            int32_t* __restrict__ topk_ids,
-                                           float* __restrict__ topk_w) {
+                                           float* __restrict__ topk_w, int32_t* hist) {
     const int lane = threadIdx.x % kWave;
     const float* row = logits + (size_t)t * E;
     // Every lane issues all its loads before the first use (indexes clamped
@@ -98,22 +100,24 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
     if (lane < k) {
         topk_ids[(size_t)t * k + lane] = my_id;
         topk_w[(size_t)t * k + lane] = ex / sum;
+        if (hist) atomicAdd(hist + my_id, 1);
     }
 }
 
 // Top-k and softmax of token t (E <= kMaxExperts) by one wavefront.
 __device__ __forceinline__ void topk_one_token(const float* __restrict__ logits, int t, int E,
                                                int k, int32_t* __restrict__ topk_ids,
-                                               float* __restrict__ topk_w) {
+                                               float* __restrict__ topk_w,
+                                               int32_t* hist = nullptr) {
     switch ((E + kWave - 1) / kWave) {
-        case 1: topk_token<1>(logits, t, E, k, topk_ids, topk_w); break;
-        case 2: topk_token<2>(logits, t, E, k, topk_ids, topk_w); break;
-        case 3: topk_token<3>(logits, t, E, k, topk_ids, topk_w); break;
-        case 4: topk_token<4>(logits, t, E, k, topk_ids, topk_w); break;
-        case 5: topk_token<5>(logits, t, E, k, topk_ids, topk_w); break;
-        case 6: topk_token<6>(logits, t, E, k, topk_ids, topk_w); break;
-        case 7: topk_token<7>(logits, t, E, k, topk_ids, topk_w); break;
-        default: topk_token<kMaxPerLane>(logits, t, E, k, topk_ids, topk_w); break;
+        case 1: topk_token<1>(logits, t, E, k, topk_ids, topk_w, hist); break;
+        case 2: topk_token<2>(logits, t, E, k, topk_ids, topk_w, hist); break;
+        case 3: topk_token<3>(logits, t, E, k, topk_ids, topk_w, hist); break;
+        case 4: topk_token<4>(logits, t, E, k, topk_ids, topk_w, hist); break;
+        case 5: topk_token<5>(logits, t, E, k, topk_ids, topk_w, hist); break;
+        case 6: topk_token<6>(logits, t, E, k, topk_ids, topk_w, hist); break;
+        case 7: topk_token<7>(logits, t, E, k, topk_ids, topk_w, hist); break;
+        default: topk_token<kMaxPerLane>(logits, t, E, k, topk_ids, topk_w, hist); break;
     }
 }
 
