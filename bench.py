@@ -48,8 +48,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "prefill512", "prefill8192", "decode40"],
-                    help="prefill2048_zipf (the headline) or decode40 (T=1, 40-layer steps)")
+                    choices=[WORKLOAD, "prefill512", "prefill8192", "decode40", "stack40"],
+                    help="prefill2048_zipf (the headline), decode40 (T=1, 40-layer steps) or "
+                         "stack40 (40 distinct layers, T=8192 in chunks of 2048, residual glue)")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer weight sets cycled")
@@ -101,6 +102,8 @@ def main():
 
     if args.workload == "decode40":
         return main_decode(args)
+    if args.workload == "stack40":
+        return main_stack(args)
 
     import numpy as np
     import torch
@@ -269,6 +272,86 @@ def main():
             "sample": f"route of all {cfg.T} tokens + forward of {ntok} tokens of layer 0 "
                       f"(dequant of the experts they use included), {c1 - c0:.1f} s",
         }
+    print(json.dumps(result), flush=True)
+
+
+def main_stack(args):
+    """Prefill through a stack of 40 distinct MoE layers (18.2 GB of int4
+    weights resident): T = 8192 tokens in 4 chunks of 2048, chunk-major; each
+    chunk runs layer after layer (route + forward), chained by the residual
+    glue (r += out; next input bf16(r / rms(r))). One step = the whole stack
+    for all 8192 tokens. Router logits per (layer, chunk) are given."""
+    import numpy as np
+    import torch
+
+    import int4_grouped_gemm_amd as L
+    from synth import inputs as S
+
+    L.load()
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS["stack40_T8192"]
+    d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, args.tile_m)
+    t_gen = time.time()
+    weights = []
+    for layer in range(cfg.layers):
+        weights.append(L.weights_from_host(S.layer_weights(cfg, layer), dev))
+        if layer % 10 == 9:
+            print(f"# {layer + 1} layers uploaded", file=sys.stderr, flush=True)
+    logits = [[torch.from_numpy(S.router_logits(cfg, layer, c)).to(dev) for c in range(cfg.chunks)]
+              for layer in range(cfg.layers)]
+    x0 = [torch.from_numpy(S.activations(cfg, c).view(np.int16)).to(dev) for c in range(cfg.chunks)]
+    r0 = [torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev) for _ in range(cfg.chunks)]
+    for c in range(cfg.chunks):  # r0 = fp32(x0): bf16 bits shifted into the high half
+        r0[c].view(torch.int32).copy_(x0[c].to(torch.int32).bitwise_left_shift(16))
+    r = torch.empty_like(r0[0])
+    x = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+    routing = L.alloc_routing(d, dev)
+    ws = L.alloc_workspace(d, dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for c in range(cfg.chunks):
+            r.copy_(r0[c])
+            L.lily_residual_norm(cfg.T, cfg.H, r, None, x, 1e-6, stream)
+            for layer in range(cfg.layers):
+                L.lily_moe_route(d, logits[layer][c], routing, stream)
+                L.lily_moe_forward(d, weights[layer], x, routing, out, ws, stream=stream)
+                L.lily_residual_norm(cfg.T, cfg.H, r, out, x, 1e-6, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    s_step = (t1 - t0) / args.steps
+    n_tok = cfg.T * cfg.chunks
+    layer_flops = 2.0 * 3 * cfg.H * cfg.F * (cfg.k + 1) * n_tok * cfg.layers
+    # every chunk-layer touches (nearly) all experts: their weights are read once per chunk
+    w_bytes = (cfg.E + 1) * 3 * cfg.H * cfg.F * (0.5 + 4.0 / 64) * cfg.chunks * cfg.layers
+    result = {
+        "metric": "MoE-layer prefill tokens/s per layer (40-layer stack, T=8192 in chunks of "
+                  "2048, int4 g64); % of HBM / MFMA peak",
+        "value": round(n_tok * cfg.layers / s_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(s_step * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "stack40", "layers": cfg.layers, "tokens": n_tok,
+                   "chunk_tokens": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "topk": cfg.k,
+                   "tile_m": args.tile_m, "glue": "r += out; x = bf16(r / rms(r))",
+                   "weights_resident_gb": round(cfg.layers * (cfg.E + 1) * 3 * cfg.H * cfg.F *
+                                                (0.5 + 4.0 / 64) / 1e9, 2)},
+        "layer": {"mfma_frac": round(layer_flops / s_step / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+                  "hbm_weight_frac": round(w_bytes / s_step / 1e9 / PEAK_HBM_GBS, 4),
+                  "prefill_tokens_per_s_whole_stack": round(n_tok / s_step, 1)},
+    }
     print(json.dumps(result), flush=True)
 
 
