@@ -18,8 +18,8 @@
 //            W_down slices of the k + 1 rows times their h, weighted by the
 //            routing weights (1 for the shared expert), summed in fp32 and
 //            written as bf16.
-// The loads of a workgroup's first phase B unit are issued together with
-// its phase A loads, so they arrive while phase A computes.
+// The loads of a workgroup's first phase B unit are issued once it has
+// counted in at the barrier, so that they arrive while it waits.
 // Row r of the layer is token r / (k + 1), slot r % (k + 1): slots 0..k-1
 // are the routed experts in top-k order, slot k the shared expert.
 #include "common.hpp"
@@ -160,7 +160,9 @@ __device__ __forceinline__ int bar_groups(int G) { return G < kBarGroups ? G : k
 __device__ __forceinline__ int bar_group_size(int G, int g) {
     return (G - g + kBarGroups - 1) / kBarGroups;
 }
-__device__ __forceinline__ void device_barrier(int32_t* bar, int32_t* grp, int32_t* err) {
+// Split in two: between barrier_arrive and barrier_wait a workgroup may
+// issue loads, which stay in flight through the wait.
+__device__ __forceinline__ void barrier_arrive(int32_t* bar, int32_t* grp) {
     const int G = gridDim.x, g = blockIdx.x % kBarGroups;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -169,7 +171,11 @@ __device__ __forceinline__ void device_barrier(int32_t* bar, int32_t* grp, int32
                                                 __HIP_MEMORY_SCOPE_AGENT);
         if (prev == bar_group_size(G, g) - 1)
             __hip_atomic_fetch_add(bar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int target = bar_groups(G);
+    }
+}
+__device__ __forceinline__ void barrier_wait(int32_t* bar, int32_t* err) {
+    if (threadIdx.x == 0) {
+        const int target = bar_groups(gridDim.x);
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(2);
@@ -179,7 +185,7 @@ __device__ __forceinline__ void device_barrier(int32_t* bar, int32_t* grp, int32
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Phase B ranges: workgroup w of G takes units [w NB / G, (w + 1) NB / G)
@@ -261,9 +267,8 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         return load_slice(rs, b_gl * kPackBlock + (b_half * kPackRows + rr) * 16,
                           b_gl * kPackBlock + kPackQ + rr * 2, 0);
     };
-    // The first phase B rounds are loaded right after the first phase A
-    // loads, so that they arrive while phase A computes. Rounds past the end
-    // are clamped onto valid data (results unused).
+    // Rounds past the end of a phase B unit are clamped onto valid data
+    // (results unused).
     Slice pb[kDecBRounds];
     float pw[kDecBRounds];
     int ph[kDecBRounds];
@@ -287,7 +292,6 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     const int UA = R * (F / 8);
     const int spr8 = H / 256;  // slices per lane per weight row
     const int l8 = lane % 8, lc = lane / 8;
-    bool b_loaded = false;
     for (int u = vw + G * wv; u < UA; u += 4 * G) {
         const int r = u / (F / 8), f0 = (u - r * (F / 8)) * 8;
         const int t = r / (k + 1), j = r - t * (k + 1);
@@ -311,10 +315,6 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
                 sg[i] = load_slice(rg, voff_q, voff_s, soff);
                 su[i] = load_slice(ru, voff_q, voff_s, soff);
             }
-            if (!b_loaded) {
-                prefetch_b();
-                b_loaded = true;
-            }
 #pragma unroll
             for (int i = 0; i < kDecASlices; ++i) {
                 if (i0 + i < spr8) {
@@ -337,8 +337,12 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
             __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h + (size_t)r * F + f0 + lane),
                                pack_bf16x2(hv, hn), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!b_loaded) prefetch_b();
-    device_barrier(a.bar, a.grp, a.err);
+    // Phase B's first rounds are loaded once this workgroup has counted in
+    // at the barrier, so that they do not compete with phase A's loads; they
+    // arrive during the wait.
+    barrier_arrive(a.bar, a.grp);
+    prefetch_b();
+    barrier_wait(a.bar, a.err);
 
     // Phase B: out[t, rows] = bf16(sum over slots j of w_j * (W_down_j rows . h_j)).
     // A thread's sum covers output row lane % 8.
