@@ -55,8 +55,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer weight sets cycled")
     ap.add_argument("--tile-m", type=int, default=128)
-    ap.add_argument("--decode-path", default="fused", choices=["fused", "layer"],
-                    help="decode40: lily_moe_decode (one launch per layer) or route + forward")
+    ap.add_argument("--decode-path", default="fused", choices=["fused", "layer", "stack"],
+                    help="decode40: lily_moe_decode (one launch per layer), route + forward, or "
+                         "lily_moe_decode_stack (the 40 layers and their residual glue in one "
+                         "launch)")
     ap.add_argument("--router", action="store_true",
                     help="start each step from x: the router projection x.Wr^T (lily_moe_router) "
                          "computes the logits inside the timed step")
@@ -383,7 +385,18 @@ def main_decode(args):
     out = torch.empty((1, cfg.H), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
 
+    if args.decode_path == "stack":
+        table = L.layer_table([weights[layer % args.layers] for layer in range(n_layers)], dev)
+        r_st = torch.empty(cfg.H, dtype=torch.float32, device=dev)
+        outs_st = torch.empty((n_layers, cfg.H), dtype=torch.int16, device=dev)
+        ids_st = torch.empty((n_layers, cfg.k), dtype=torch.int32, device=dev)
+        w_st = torch.empty((n_layers, cfg.k), dtype=torch.float32, device=dev)
+
     def step(i):
+        if args.decode_path == "stack":
+            L.lily_moe_decode_stack(d, n_layers, table, logits[i], xs[i], r_st, outs_st, ids_st,
+                                    w_st, routing.sched, ws, 1e-6, stream)
+            return
         for layer in range(n_layers):
             w = weights[layer % args.layers]
             if args.decode_path == "fused":
@@ -415,8 +428,10 @@ def main_decode(args):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode40", "T": 1, "H": cfg.H, "F": cfg.F, "E": cfg.E,
                    "topk": cfg.k, "layers_per_step": n_layers, "layer_weight_sets": args.layers,
-                   "path": "lily_moe_decode" if args.decode_path == "fused"
-                   else "lily_moe_route + lily_moe_forward (tile_m 32)"},
+                   "path": {"fused": "lily_moe_decode, one launch per layer",
+                            "layer": "lily_moe_route + lily_moe_forward (tile_m 32)",
+                            "stack": "lily_moe_decode_stack: 40 layers and the residual glue "
+                                     "in one launch"}[args.decode_path]},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "whole layer"},

@@ -278,10 +278,8 @@ int lily_moe_forward_bf16(const lily_moe_dims* dims, const lily_moe_weights* bf1
 
 /* Route and forward of one MoE layer for a few tokens (T <= 4, decode) in
    one launch: the routing of lily_moe_route (same ids and weights) and the
-   output of lily_moe_forward up to rounding: the weights enter as the exact
-   fp32 values scale * q + bias (scale and bias applied to each 32-weight dot
-   product) instead of being rounded to bf16 first, and fp32 sums run in
-   another order. Every weight of the k routed experts and of the
+   output of lily_moe_forward up to the order of the fp32 sums (the same
+   bf16 weights bf16(scale * q + bias), bf16 h and fp32 accumulation). Every weight of the k routed experts and of the
    shared expert is read once, spread over one workgroup per compute unit
    as matrix-vector products: gate/up by one wavefront per (row, 8 features)
    over all of K, which forms that part of h itself; one device-wide
@@ -301,6 +299,33 @@ int lily_moe_forward_bf16(const lily_moe_dims* dims, const lily_moe_weights* bf1
 int lily_moe_decode(const lily_moe_dims* dims, const lily_moe_weights* weights,
                     const float* logits, const uint16_t* x, const lily_moe_routing* routing,
                     uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Batch-1 decode through a stack of MoE layers in one launch (T = 1): for
+   l = 0 .. n_layers - 1, x_l = bf16(r_l / sqrt(mean(r_l^2) + eps)) with
+   r_0 = x0, out_l = the MoE layer l of lily_moe_decode on x_l, and
+   r_{l+1} = r_l + out_l (fp32): the chain of lily_moe_decode and
+   lily_residual_norm launches, in one launch whose workgroups (one per
+   compute unit, all resident, as for lily_moe_decode) pass two device-wide
+   barriers per layer. The next layer's top-k and gate/up weight loads are
+   issued while the current layer's down phase runs (the pages run a decode
+   step as one concurrent pass: Lily articles, section "Decode").
+   layers: device array of n_layers lily_moe_weights (packed stacks, as for
+   lily_moe_decode); logits fp32 [n_layers][E]; x0 bf16 [H]; r fp32 [H]
+   (ignored on entry, r_{n_layers} on exit); outs bf16 [n_layers][H] (each
+   layer's output); topk_ids int32 and topk_w fp32 [n_layers][topk] (each
+   layer's routing); sched: as in lily_moe_routing (its barrier counters are
+   zero on entry and left zero; sched[30] is set to 1 if a barrier wait gave
+   up after half a second, which makes the outputs invalid).
+   Needs T = 1, H a multiple of 512 (at most 2048), F a multiple of 256 with
+   (topk + 1) * F <= 16384, and (topk + 1) * F / 8 at most four per compute
+   unit. workspace: lily_moe_workspace_bytes(dims) bytes.
+   Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED, LILY_ERR_WORKSPACE,
+   LILY_ERR_HIP. */
+int lily_moe_decode_stack(const lily_moe_dims* dims, int32_t n_layers,
+                          const lily_moe_weights* layers, const float* logits, const uint16_t* x0,
+                          float* r, uint16_t* outs, int32_t* topk_ids, float* topk_w,
+                          int32_t* sched, float eps, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Residual stream between stacked MoE layers (the pages describe a stack of
    layers but not this glue; the reading is a pre-norm residual with a

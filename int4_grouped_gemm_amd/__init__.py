@@ -26,7 +26,8 @@ LILY_ERR_HIP = -4
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
            "lily_w4_pack", "lily_moe_router", "lily_moe_route", "lily_moe_route_host",
            "lily_moe_forward", "lily_moe_dequant", "lily_moe_forward_bf16", "lily_moe_gate_up",
-           "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_residual_norm",
+           "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_moe_decode_stack",
+           "lily_residual_norm",
            "lily_last_error")
 LILY_SCHED_INTS = 1056 + 64 * 512 + 1
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
@@ -119,6 +120,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_moe_decode.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
                                     ctypes.c_void_p, P(LilyMoeRouting), ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.lily_moe_decode_stack.restype = ctypes.c_int
+    lib.lily_moe_decode_stack.argtypes = [P(LilyMoeDims), ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
     lib.lily_residual_norm.restype = ctypes.c_int
     lib.lily_residual_norm.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
@@ -339,6 +346,23 @@ def lily_moe_decode(d: LilyMoeDims, weights: Weights, logits, x, routing: Routin
     rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(logits), _ptr(x),
                              ctypes.byref(routing.c()), _ptr(out), _ptr(workspace),
                              _ws_bytes(workspace), _stream(stream))
+    _check(rc, lib)
+
+
+def layer_table(weights: list, device="cuda") -> torch.Tensor:
+    """Device array of lily_moe_weights (six pointers per layer) for
+    lily_moe_decode_stack; the Weights objects must outlive it."""
+    rows = [[getattr(w, n).data_ptr() for n in WEIGHT_FIELDS] for w in weights]
+    return torch.tensor(rows, dtype=torch.int64).to(device)
+
+
+def lily_moe_decode_stack(d: LilyMoeDims, n_layers: int, layers, logits, x0, r, outs, topk_ids,
+                          topk_w, sched, workspace, eps: float = 1e-6, stream=None) -> None:
+    """T = 1 decode through n_layers MoE layers in one launch (see the header)."""
+    lib = load()
+    rc = lib.lily_moe_decode_stack(ctypes.byref(d), n_layers, _ptr(layers), _ptr(logits), _ptr(x0),
+                                   _ptr(r), _ptr(outs), _ptr(topk_ids), _ptr(topk_w), _ptr(sched),
+                                   eps, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
     _check(rc, lib)
 
 

@@ -34,6 +34,11 @@ int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_mo
                 int max_blocks, const ForwardWorkspace& ws, hipStream_t stream, bool w4);
 int launch_dequant(const void* packed, int n, int N, int K, const int32_t* counts, void* out,
                    hipStream_t stream);
+int decode_stack_supported(const lily_moe_dims& d, int n_layers);
+int launch_decode_stack(const lily_moe_dims& d, int n_layers, const lily_moe_weights* layers,
+                        const float* logits, const uint16_t* x0, float* r, uint16_t* outs,
+                        int32_t* topk_ids, float* topk_w, int32_t* sched, float eps,
+                        void* workspace, hipStream_t stream);
 int launch_combine(const lily_moe_dims& d, const ForwardWorkspace& ws, const lily_moe_routing& r,
                    uint16_t* out, hipStream_t stream);
 size_t forward_workspace_bytes(const lily_moe_dims& d, int max_blocks);
@@ -350,6 +355,28 @@ int lily_residual_norm(int32_t T, int32_t H, float* r, const uint16_t* out, uint
     if (out && !aligned16(out))
         return set_error(LILY_ERR_INVALID_ARG, "out is not 16-byte aligned");
     return launch_residual_norm(T, H, r, out, x_next, eps, reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_decode_stack(const lily_moe_dims* dims, int32_t n_layers,
+                          const lily_moe_weights* layers, const float* logits, const uint16_t* x0,
+                          float* r, uint16_t* outs, int32_t* topk_ids, float* topk_w,
+                          int32_t* sched, float eps, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if ((rc = decode_stack_supported(*dims, n_layers))) return rc;
+    REQUIRE_PTR(layers);
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(x0);
+    REQUIRE_PTR(r);
+    REQUIRE_PTR(outs);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(sched);
+    if (!(eps >= 0.0f)) return set_error(LILY_ERR_INVALID_ARG, "eps must be >= 0");
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    return launch_decode_stack(*dims, n_layers, layers, logits, x0, r, outs, topk_ids, topk_w,
+                               sched, eps, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 const char* lily_last_error(void) { return g_last_error; }

@@ -37,7 +37,6 @@ constexpr int kDecBRounds = 6;       // phase B rounds per wavefront loaded at o
 constexpr int kDecLdsWords = 8192;   // LDS: x rows (phase A) or h rows (phase B), bf16 pairs
 constexpr int kDecXChunks = 8;       // x 16-byte chunks staged per thread: T * H <= 16384
 constexpr int kDecHChunks = kDecLdsWords / 4 / kDecThreads;  // h chunks staged per thread
-constexpr int kDecSums = kDecLdsWords / 16;  // sums of 32 staged values
 constexpr int kDecPiece = 8;         // output rows per phase B unit
 constexpr long kSpinTicks = 50000000;  // device-wide barrier wait limit: 0.5 s at 100 MHz
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor: raw, 32-bit data format
@@ -99,44 +98,37 @@ __device__ __forceinline__ u32x4 permute_chunk(u32x4 p) {
     return o;
 }
 
-// Dot product of a slice's 32 weights w = scale * q + bias with 32 staged
-// values v (16 permuted words) whose sum is vsum: scale * sum(q v) +
-// bias * vsum. The nibbles j and j + 4 of a weight word become the bf16 pair
-// (128 + q_j, 128 + q_j+4) with one byte permute each (exact: the exponent
-// byte 0x43 sets the scale to 1 on [128, 256)), so that
-// sum(q v) = sum((128 + q) v) - 128 vsum comes from bf16 dot2 instructions.
-// The weights enter exactly (fp32 scale and bias), not rounded to bf16 as in
-// the GEMMs.
-__device__ __forceinline__ float dot_slice(const Slice& s, const uint32_t* v, float vsum) {
+// Dot product of a slice's 32 weights with 32 staged values v (16 permuted
+// words). Each weight is rebuilt as w = bf16(scale * q + bias) exactly as
+// the grouped GEMMs do (one fp32 fma on q * 2^-9 from v_cvt_pk_f32_fp8, then
+// RNE to bf16), and the bf16 pairs (w_j, w_j+4) meet the staged words in
+// bf16 dot2 instructions with fp32 accumulation. (Using the exact fp32
+// weights instead, applying scale and bias to each 32-weight sum, is cheaper
+// but misses the tolerance on tokens whose layer output is small next to
+// its terms: a systematic 2^-9 per weight then survives the cancellation.)
+__device__ __forceinline__ float dot_slice(const Slice& s, const uint32_t* v) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const float s512 = bf16_bits_to_float(s.sc) * 512.0f, b = bf16_bits_to_float(s.bi);
     float acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const uint32_t lo = s.q[w] & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
         const uint32_t hi = (s.q[w] >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
-        // bytes: 0-3 from the second operand, 4-7 from the first (0x43 each)
-        const uint32_t wt[4] = {__builtin_amdgcn_perm(0x43434343u, lo, 0x04020400u),   // 0, 4
-                                __builtin_amdgcn_perm(0x43434343u, hi, 0x04020400u),   // 1, 5
-                                __builtin_amdgcn_perm(0x43434343u, lo, 0x04030401u),   // 2, 6
-                                __builtin_amdgcn_perm(0x43434343u, hi, 0x04030401u)};  // 3, 7
+        const f2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+        const f2 e46 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+        const f2 e13 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+        const f2 e57 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+        const uint32_t wt[4] = {pack_bf16x2(fmaf(s512, e02[0], b), fmaf(s512, e46[0], b)),   // 0, 4
+                                pack_bf16x2(fmaf(s512, e13[0], b), fmaf(s512, e57[0], b)),   // 1, 5
+                                pack_bf16x2(fmaf(s512, e02[1], b), fmaf(s512, e46[1], b)),   // 2, 6
+                                pack_bf16x2(fmaf(s512, e13[1], b), fmaf(s512, e57[1], b))};  // 3, 7
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wt[e]),
                                                   __builtin_bit_cast(bf16x2, v[4 * w + e]), acc,
                                                   false);
     }
-    const float scale = bf16_bits_to_float(s.sc), bias = bf16_bits_to_float(s.bi);
-    return fmaf(scale, acc, fmaf(-128.0f, scale, bias) * vsum);
-}
-
-// Sum of the 32 bf16 values in 16 LDS words (fp32).
-__device__ __forceinline__ float sum32(const uint32_t* v) {
-    float a = 0.0f, b = 0.0f;
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-        a += bf16_bits_to_float(v[n] & 0xFFFFu);
-        b += bf16_bits_to_float(v[n] >> 16);
-    }
-    return a + b;
+    return acc;
 }
 
 // Workgroup barrier that waits for this thread's LDS accesses only: global
@@ -161,21 +153,33 @@ __device__ __forceinline__ int bar_group_size(int G, int g) {
     return (G - g + kBarGroups - 1) / kBarGroups;
 }
 // Split in two: between barrier_arrive and barrier_wait a workgroup may
-// issue loads, which stay in flight through the wait.
-__device__ __forceinline__ void barrier_arrive(int32_t* bar, int32_t* grp) {
+// issue loads, which stay in flight through the wait. The counters only
+// grow within a launch, so one launch can pass several barriers: the
+// instance-th barrier (from 0) is passed when `bar` reaches (instance + 1)
+// groups, and a group counts in when its counter reaches a multiple of the
+// group's size. Every workgroup arrives at every instance.
+// lead: the thread that counts the workgroup in; every wavefront waits for
+// its own stores first, or only the lead's wavefront when it made all of
+// the stores the barrier publishes (the others' loads stay in flight).
+__device__ __forceinline__ void barrier_arrive(int32_t* bar, int32_t* grp, int lead = 0,
+                                               bool all_stored = true) {
     const int G = gridDim.x, g = blockIdx.x % kBarGroups;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
+    if (all_stored || threadIdx.x / kWave == lead / kWave)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (threadIdx.x == lead) {
         const int prev = __hip_atomic_fetch_add(grp + g * kBarLine, 1, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == bar_group_size(G, g) - 1)
+        if ((prev + 1) % bar_group_size(G, g) == 0)
             __hip_atomic_fetch_add(bar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
-__device__ __forceinline__ void barrier_wait(int32_t* bar, int32_t* err) {
-    if (threadIdx.x == 0) {
-        const int target = bar_groups(gridDim.x);
+// poll: the polling thread. Its loads return in order, so it should belong
+// to a wavefront with no loads in flight.
+__device__ __forceinline__ void barrier_wait(int32_t* bar, int32_t* err, int instance = 0,
+                                             int poll = 0) {
+    if (threadIdx.x == poll) {
+        const int target = (instance + 1) * bar_groups(gridDim.x);
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(2);
@@ -188,6 +192,28 @@ __device__ __forceinline__ void barrier_wait(int32_t* bar, int32_t* err) {
     lds_barrier();
 }
 
+// Every workgroup has passed every barrier wait before it counts out here,
+// in the same two levels: the last of a group clears the group's counters,
+// the last group clears `bar` for the next launch. lead: the thread that
+// made the workgroup's last arrival, so that its count-out follows it.
+__device__ __forceinline__ void barrier_exit(int32_t* bar, int32_t* grp, int lead = 0) {
+    const int G = gridDim.x;
+    if (threadIdx.x == lead) {
+        const int g = blockIdx.x % kBarGroups;
+        int32_t* gc = grp + g * kBarLine;
+        if (__hip_atomic_fetch_add(gc + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            bar_group_size(G, g) - 1) {
+            __hip_atomic_store(gc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(gc + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__hip_atomic_fetch_add(bar + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                bar_groups(G) - 1) {
+                __hip_atomic_store(bar, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(bar + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
 // Phase B ranges: workgroup w of G takes units [w NB / G, (w + 1) NB / G)
 // (NB * G < 2^31 on the host's checks).
 __device__ __forceinline__ int range_begin(int w, int nb, int g) { return (unsigned)(w * nb) / (unsigned)g; }
@@ -196,7 +222,6 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     __shared__ int32_t s_ids[kDecodeMaxT * kMaxTopk];
     __shared__ float s_w[kDecodeMaxT * kMaxTopk];
     __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDecLdsWords];
-    __shared__ float s_vsum[kDecSums];  // sums of 32 consecutive staged values
     __shared__ float s_bred[kDecThreads / kWave][kDecPiece];
 
     const int tid = threadIdx.x;
@@ -232,8 +257,6 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         const int c = tid + n * kDecThreads;
         if (c * 4 < x_words) *reinterpret_cast<u32x4*>(s_buf + 4 * c) = permute_chunk(xr[n]);
     }
-    __syncthreads();
-    for (int q = tid; q < x_words / 16; q += kDecThreads) s_vsum[q] = sum32(s_buf + 16 * q);
     __syncthreads();
     if (wg == 0 && tid < a.T * k) {
         a.topk_ids[tid] = s_ids[tid];
@@ -319,9 +342,8 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
             for (int i = 0; i < kDecASlices; ++i) {
                 if (i0 + i < spr8) {
                     const int xo = xbase + (i0 + i) * 128;
-                    const float vs = s_vsum[xo / 16];
-                    ag += dot_slice(sg[i], s_buf + xo, vs);
-                    au += dot_slice(su[i], s_buf + xo, vs);
+                    ag += dot_slice(sg[i], s_buf + xo);
+                    au += dot_slice(su[i], s_buf + xo);
                 }
             }
         }
@@ -370,8 +392,6 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
                 if (c < h_words / 4) *reinterpret_cast<u32x4*>(s_buf + 4 * c) = permute_chunk(hr[n]);
             }
             __syncthreads();
-            for (int q = tid; q < h_words / 16; q += kDecThreads) s_vsum[q] = sum32(s_buf + 16 * q);
-            __syncthreads();
             t_staged = t;
         }
         float acc = 0.0f;
@@ -384,7 +404,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int n = 0; n < kDecBRounds; ++n)
                 if (wv + 4 * (n0 + n) < NRB)
-                    acc = fmaf(pw[n], dot_slice(pb[n], s_buf + ph[n], s_vsum[ph[n] / 16]), acc);
+                    acc = fmaf(pw[n], dot_slice(pb[n], s_buf + ph[n]), acc);
         }
         // the next unit's first rounds, in flight during this unit's sums
         if (u + 1 < ub1) {
@@ -408,23 +428,328 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
         __syncthreads();
     }
 
-    // Every workgroup has passed the barrier before it counts out here, in
-    // the same two levels: the last of a group clears the group's counters,
-    // the last group clears `bar` for the next launch.
-    if (tid == 0) {
-        const int g = wg % kBarGroups;
-        int32_t* gc = a.grp + g * kBarLine;
-        if (__hip_atomic_fetch_add(gc + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            bar_group_size(G, g) - 1) {
-            __hip_atomic_store(gc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(gc + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (__hip_atomic_fetch_add(a.bar + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                bar_groups(G) - 1) {
-                __hip_atomic_store(a.bar, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.bar + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    barrier_exit(a.bar, a.grp);
+}
+
+constexpr int kStackMaxIds = 2048;  // n_layers * topk routing entries held in LDS
+
+// Batch-1 decode through a stack of MoE layers in one launch (T = 1): the
+// layers of one decode step chained by the residual glue (r_0 = x_0;
+// x_l = bf16(r_l / rms(r_l)); r_{l+1} = r_l + out_l), which the pages run as
+// one concurrent pass per step (Lily articles, section "Decode"). Per layer
+// the phases of moe_decode_kernel, with two device-wide barriers: after the
+// gate/up phase (h complete) and after the down phase (out and r complete).
+// The launch routes every layer first (the logits are inputs); the next
+// layer's gate/up weight loads do not depend on this layer's output, so they
+// are issued between this layer's h barrier arrival and wait and stream
+// while this layer's down phase runs.
+struct StackArgs {
+    int L, H, F, E, k;
+    const lily_moe_weights* layers;  // device array [L]
+    const float* logits;             // [L][E]
+    const uint16_t* x0;              // [H] bf16
+    float* r;                        // [H] fp32 residual; r_L on exit
+    uint16_t* outs;                  // [L][H] bf16 layer outputs
+    int32_t* topk_ids;               // [L][k]
+    float* topk_w;                   // [L][k]
+    uint16_t* h;                     // kDecXcds copies of [k + 1][F] bf16
+    float* rr;                       // kDecXcds copies of r_l [H]
+    float eps;
+    int32_t* bar;
+    int32_t* grp;
+    int32_t* err;
+};
+
+__global__ void __launch_bounds__(kDecThreads) moe_decode_stack_kernel(StackArgs a) {
+    __shared__ int32_t s_ids[kStackMaxIds];  // [L][k]: every layer's routing
+    __shared__ float s_w[kStackMaxIds];
+    __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDecLdsWords];
+    __shared__ float s_bred[kDecThreads / kWave][kDecPiece];
+    __shared__ float s_part[kDecThreads / kWave];
+    __shared__ float s_r[kDecASlices * 256];  // r_l (H <= 2048)
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int G = gridDim.x;
+    const int wg = blockIdx.x;
+    const int vw = G % kDecXcds == 0 ? (wg % kDecXcds) * (G / kDecXcds) + wg / kDecXcds : wg;
+    // r and h are kept in one copy per XCD (written by their producers to
+    // all copies): every workgroup reads them with device-coherent loads,
+    // which go past the XCD's L2, and 256 readers of one copy load its
+    // memory channels with the same lines.
+    const int xc = wg % kDecXcds;
+    const int k = a.k, E = a.E, H = a.H, F = a.F;
+    const int R = k + 1;
+    const int nkg = H / kGroup, nsf = F / kPackRows, nkgF = F / kGroup, nsH = H / kPackRows;
+
+    // Phase A unit of this wavefront (at most one: the host checks
+    // R * F / 8 <= 4 G): unit u = (row j, features f0 .. f0 + 7).
+    const int u = vw + G * wv;
+    const bool has_unit = u < R * (F / 8);
+    const int uj = has_unit ? u / (F / 8) : 0;
+    const int f0 = has_unit ? (u - uj * (F / 8)) * 8 : 0;
+    const bool ush = uj == k;
+    const int l8 = lane % 8, lc = lane / 8;
+    const int spr8 = H / 256;  // <= kDecASlices (host check)
+    const int rr = f0 % kPackRows + l8;
+    const int voff_q = (lc >> 1) * kPackBlock + ((lc & 1) * kPackRows + rr) * 16;
+    const int voff_s = (lc >> 1) * kPackBlock + kPackQ + rr * 2;
+    const int xbase = (lc >> 1) * 32 + (lc & 1) * 16;
+    Slice sg[kDecASlices], su[kDecASlices];
+
+    // Phase B unit range (output rows of 8).
+    const int UB = H / kDecPiece;
+    const int ub0 = range_begin(vw, UB, G), ub1 = range_begin(vw + 1, UB, G);
+    const int nq = nkgF / 4;
+    const int NRB = R * nq;
+    const int b_gl = lane / 16, b_half = (lane / 8) % 2, b_row = lane % kDecPiece;
+    Slice pb[kDecBRounds];
+    float pw[kDecBRounds];
+    int ph[kDecBRounds];
+
+    // Routing of every layer first: its logits are inputs of the launch.
+    // Wavefront v takes layers v, v + 4, ...; workgroup 0 writes them out.
+    for (int l = wave; l < a.L; l += kDecThreads / kWave)
+        topk_one_token(a.logits, l, E, k, s_ids, s_w);
+    lds_barrier();
+    if (wg == 0)
+        for (int i = tid; i < a.L * k; i += kDecThreads) {
+            a.topk_ids[i] = s_ids[i];
+            a.topk_w[i] = s_w[i];
+        }
+    // Gate/up weight loads of this wavefront's unit for layer l.
+    auto issue_a = [&](int l) {
+        if (!has_unit) return;
+        const lily_moe_weights& w = a.layers[l];
+        const int e = ush ? 0 : s_ids[l * k + uj];
+        const size_t seg = ((size_t)e * nsf + f0 / kPackRows) * nkg * kPackBlock;
+        const Rsrc rg = make_rsrc(static_cast<const char*>(ush ? w.sh_gate : w.gate) + seg,
+                                  nkg * kPackBlock);
+        const Rsrc ru = make_rsrc(static_cast<const char*>(ush ? w.sh_up : w.up) + seg,
+                                  nkg * kPackBlock);
+#pragma unroll
+        for (int i = 0; i < kDecASlices; ++i) {
+            const int soff = min(i, spr8 - 1) * 4 * kPackBlock;
+            sg[i] = load_slice(rg, voff_q, voff_s, soff);
+            su[i] = load_slice(ru, voff_q, voff_s, soff);
+        }
+    };
+    // One phase B round: slot j = rho / nq, groups 4 gq .. 4 gq + 3 of unit ub.
+    auto b_round = [&](int l, int ub, int rho, float& wj, int& hoff) -> Slice {
+        const lily_moe_weights& w = a.layers[l];
+        const int r0 = ub * kDecPiece;
+        const int j = rho / nq, gq = rho - j * nq;
+        const bool sh = (j == k);
+        const int e = sh ? 0 : s_ids[l * k + j];
+        wj = sh ? 1.0f : s_w[l * k + j];
+        hoff = (j * F + (4 * gq + b_gl) * kGroup + b_half * 32) / 2;
+        const char* stack = static_cast<const char*>(sh ? w.sh_down : w.down);
+        const Rsrc rs = make_rsrc(
+            stack + ((size_t)(e * nsH + r0 / kPackRows) * nkgF + 4 * gq) * kPackBlock,
+            4 * kPackBlock);
+        const int rrb = r0 % kPackRows + b_row;
+        return load_slice(rs, b_gl * kPackBlock + (b_half * kPackRows + rrb) * 16,
+                          b_gl * kPackBlock + kPackQ + rrb * 2, 0);
+    };
+    const int ub_first = ub0 < ub1 ? ub0 : 0;
+
+    // The last wavefront loads r and h for the workgroup, stores each
+    // layer's out and r, counts the workgroup in and polls: it holds no
+    // gate/up unit when units fill at most three wavefronts per workgroup,
+    // so none of its loads queues behind gate/up loads.
+    constexpr int kLeadWave = kDecThreads / kWave - 1;
+    constexpr int kLead = kLeadWave * kWave;
+    int inst = 0;  // barrier instances passed or arrived at
+    issue_a(0);
+    for (int l = 0; l < a.L; ++l) {
+        if (l > 0) barrier_wait(a.bar, a.err, inst - 1, kLead);  // layer l - 1's out and r
+
+        // x_l = bf16(r_l / sqrt(mean(r_l^2) + eps)), r_0 = x_0. The lead
+        // wavefront, which has no gate/up loads in flight (a load returns
+        // after every earlier one of its wavefront), brings r_l into LDS;
+        // then thread t takes elements 4t + 1024 i .. + 3 and the sum of
+        // squares runs in the order of residual_norm_kernel (same result bit
+        // for bit).
+        {
+            if (wave == kLeadWave) {
+                // all of r in flight at once: pairs of floats, 16 per lane
+                constexpr int kPairs = kDecASlices * 256 / 2 / kWave;
+                uint64_t t[kPairs];
+#pragma unroll
+                for (int j = 0; j < kPairs; ++j) {
+                    const int p = min(lane + j * kWave, H / 2 - 1);
+                    t[j] = l == 0 ? (uint64_t)reinterpret_cast<const uint32_t*>(a.x0)[p]
+                                  : __hip_atomic_load(
+                                        reinterpret_cast<const uint64_t*>(a.rr + (size_t)xc * H) + p,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int j = 0; j < kPairs; ++j) {
+                    const int p = lane + j * kWave;
+                    if (p < H / 2) {
+                        if (l == 0) {  // two bf16 of x0
+                            s_r[2 * p] = bf16_bits_to_float((uint32_t)t[j] & 0xFFFFu);
+                            s_r[2 * p + 1] = bf16_bits_to_float(((uint32_t)t[j]) >> 16);
+                        } else {
+                            s_r[2 * p] = __uint_as_float((uint32_t)t[j]);
+                            s_r[2 * p + 1] = __uint_as_float((uint32_t)(t[j] >> 32));
+                        }
+                    }
+                }
+            }
+            lds_barrier();
+            float v[kDecXChunks][4];
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kDecXChunks; ++i) {
+                const int n = tid * 4 + i * kDecThreads * 4;
+                if (n < H) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v[i][c] = s_r[n + c];
+                    ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] +
+                          v[i][3] * v[i][3];
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+            if (lane == 0) s_part[wave] = ss;
+            lds_barrier();
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kDecThreads / kWave; ++w) tot += s_part[w];
+            const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
+#pragma unroll
+            for (int i = 0; i < kDecXChunks; ++i) {
+                const int n = tid * 4 + i * kDecThreads * 4;
+                if (n < H) {
+                    s_buf[n / 2] = pack_bf16x2(v[i][0] * inv, v[i][1] * inv);
+                    s_buf[n / 2 + 1] = pack_bf16x2(v[i][2] * inv, v[i][3] * inv);
+                }
+            }
+            lds_barrier();
+            // natural bf16 pairs -> the permuted chunks dot_slice reads
+            for (int c = tid; c < H / 8; c += kDecThreads) {
+                const u32x4 p = *reinterpret_cast<const u32x4*>(s_buf + 4 * c);
+                *reinterpret_cast<u32x4*>(s_buf + 4 * c) = permute_chunk(p);
+            }
+            lds_barrier();
+        }
+
+        // This layer's down weights: they arrive during phase A and its
+        // barrier.
+#pragma unroll
+        for (int n = 0; n < kDecBRounds; ++n)
+            pb[n] = b_round(l, ub_first, min(wv + 4 * n, NRB - 1), pw[n], ph[n]);
+        // Phase A of layer l: the unit's loads were issued earlier.
+        if (has_unit) {
+            float ag = 0.0f, au = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kDecASlices; ++i) {
+                if (i < spr8) {
+                    const int xo = xbase + i * 128;
+                    ag += dot_slice(sg[i], s_buf + xo);
+                    au += dot_slice(su[i], s_buf + xo);
+                }
+            }
+            ag += __shfl_xor(ag, 8);
+            ag += __shfl_xor(ag, 16);
+            ag += __shfl_xor(ag, 32);
+            au += __shfl_xor(au, 8);
+            au += __shfl_xor(au, 16);
+            au += __shfl_xor(au, 32);
+            const float hv = silu(ag) * au;
+            const float hn = __shfl_down(hv, 1);
+            if (lane < 8 && (lane & 1) == 0) {
+                const uint32_t hw = pack_bf16x2(hv, hn);
+#pragma unroll
+                for (int c = 0; c < kDecXcds; ++c)
+                    __hip_atomic_store(
+                        reinterpret_cast<uint32_t*>(a.h + ((size_t)c * R + uj) * F + f0 + lane), hw,
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        barrier_arrive(a.bar, a.grp, kLead, true);
+        const int inst_h = inst++;
+        // While the others finish phase A: the next layer's gate/up weights,
+        // which stream during this layer's down phase.
+        if (l + 1 < a.L) issue_a(l + 1);
+        barrier_wait(a.bar, a.err, inst_h, kLead);
+
+        // Phase B of layer l: out_l rows and r_{l+1} = r_l + out_l. h comes
+        // into LDS through the lead wavefront, for the same reason as r.
+        const int h_words = R * F / 2;
+        if (wave == kLeadWave) {
+            // 16-byte chunks as two 8-byte loads, 12 chunks per lane in flight
+            const uint64_t* hg = reinterpret_cast<const uint64_t*>(a.h + (size_t)xc * R * F);
+            constexpr int kC = 12;
+            for (int c0 = lane; c0 < h_words / 4; c0 += kC * kWave) {
+                uint64_t t[kC][2];
+#pragma unroll
+                for (int j = 0; j < kC; ++j) {
+                    const int c = min(c0 + j * kWave, h_words / 4 - 1);
+                    t[j][0] = __hip_atomic_load(hg + 2 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    t[j][1] = __hip_atomic_load(hg + 2 * c + 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int j = 0; j < kC; ++j)
+                    if (c0 + j * kWave < h_words / 4) {
+                        const u32x4 hr = {(uint32_t)t[j][0], (uint32_t)(t[j][0] >> 32),
+                                          (uint32_t)t[j][1], (uint32_t)(t[j][1] >> 32)};
+                        *reinterpret_cast<u32x4*>(s_buf + 4 * (c0 + j * kWave)) = permute_chunk(hr);
+                    }
+            }
+        }
+        lds_barrier();
+        for (int ub = ub0; ub < ub1; ++ub) {
+            float acc = 0.0f;
+            for (int n0 = 0; wv + 4 * n0 < NRB; n0 += kDecBRounds) {
+                if (n0 > 0) {
+#pragma unroll
+                    for (int n = 0; n < kDecBRounds; ++n)
+                        pb[n] = b_round(l, ub, min(wv + 4 * (n0 + n), NRB - 1), pw[n], ph[n]);
+                }
+#pragma unroll
+                for (int n = 0; n < kDecBRounds; ++n)
+                    if (wv + 4 * (n0 + n) < NRB)
+                        acc = fmaf(pw[n], dot_slice(pb[n], s_buf + ph[n]), acc);
+            }
+            if (ub + 1 < ub1) {
+#pragma unroll
+                for (int n = 0; n < kDecBRounds; ++n)
+                    pb[n] = b_round(l, ub + 1, min(wv + 4 * n, NRB - 1), pw[n], ph[n]);
+            }
+            acc += __shfl_xor(acc, 8);
+            acc += __shfl_xor(acc, 16);
+            acc += __shfl_xor(acc, 32);
+            if (lane < kDecPiece) s_bred[wave][lane] = acc;
+            lds_barrier();
+            if (tid >= kLead && tid < kLead + kDecPiece) {
+                float o = 0.0f;
+#pragma unroll
+                for (int v = 0; v < kDecThreads / kWave; ++v) o += s_bred[v][tid - kLead];
+                const int n = ub * kDecPiece + tid - kLead;
+                const uint16_t ob = float_to_bf16_bits(o);
+                a.outs[(size_t)l * H + n] = ob;
+                const float rprev = l == 0 ? bf16_bits_to_float(a.x0[n])
+                                           : __hip_atomic_load(a.rr + (size_t)xc * H + n,
+                                                               __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+                const float rn = rprev + bf16_bits_to_float(ob);
+#pragma unroll
+                for (int c = 0; c < kDecXcds; ++c)
+                    __hip_atomic_store(a.rr + (size_t)c * H + n, rn, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                if (l == a.L - 1) a.r[n] = rn;
+            }
+            lds_barrier();
+        }
+        barrier_arrive(a.bar, a.grp, kLead, false);
+        ++inst;
     }
+    barrier_exit(a.bar, a.grp, kLead);
 }
 
 // One workgroup per compute unit, at most kDecMaxGrid.
@@ -441,10 +766,17 @@ static int decode_grid() {
     return cus[dev] < kDecMaxGrid ? cus[dev] : kDecMaxGrid;
 }
 
-// h, bf16 [T (k + 1), F].
+// lily_moe_decode: h, bf16 [T (k + 1), F]. lily_moe_decode_stack (T = 1):
+// kDecXcds copies of h, then kDecXcds copies of r [H] fp32.
+static size_t stack_h_bytes(const lily_moe_dims& d) {
+    return ((size_t)kDecXcds * (d.topk + 1) * d.F * sizeof(uint16_t) + 255) & ~(size_t)255;
+}
 size_t decode_workspace_bytes(const lily_moe_dims& d) {
     if (d.T > kDecodeMaxT) return 0;
-    return (size_t)d.T * (d.topk + 1) * d.F * sizeof(uint16_t);
+    const size_t one = (size_t)d.T * (d.topk + 1) * d.F * sizeof(uint16_t);
+    if (d.T != 1) return one;
+    const size_t stack = stack_h_bytes(d) + (size_t)kDecXcds * d.H * sizeof(float);
+    return one > stack ? one : stack;
 }
 
 constexpr int kDecMaxH = 4096;  // x of kDecodeMaxT tokens fills the LDS staging area
@@ -496,6 +828,58 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
     // device-wide barrier relies on.
     hipLaunchKernelGGL(moe_decode_kernel, dim3((unsigned)g), dim3(kDecThreads), 0, stream, a);
     return check_launch("decode");
+}
+
+int decode_stack_supported(const lily_moe_dims& d, int n_layers) {
+    if (n_layers < 1) return set_error(LILY_ERR_INVALID_ARG, "n_layers = %d must be >= 1", n_layers);
+    if ((long)n_layers * d.topk > kStackMaxIds)
+        return set_error(LILY_ERR_UNSUPPORTED, "n_layers * topk = %ld exceeds %d",
+                         (long)n_layers * d.topk, kStackMaxIds);
+    if (d.T != 1)
+        return set_error(LILY_ERR_UNSUPPORTED, "T = %d; lily_moe_decode_stack serves T = 1", d.T);
+    if (d.H % (2 * kDecThreads) || d.H > kDecASlices * 256)
+        return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 512, at most %d",
+                         d.H, kDecASlices * 256);
+    if (d.F % (4 * kGroup) || (long)(d.topk + 1) * d.F > 2L * kDecLdsWords)
+        return set_error(LILY_ERR_UNSUPPORTED,
+                         "F = %d must be a multiple of 256 with (topk + 1) * F <= %d", d.F,
+                         2 * kDecLdsWords);
+    const long units = (long)(d.topk + 1) * (d.F / 8);
+    if (units > 4L * decode_grid())
+        return set_error(LILY_ERR_UNSUPPORTED,
+                         "(topk + 1) * F / 8 = %ld gate/up units exceed 4 per compute unit", units);
+    return LILY_OK;
+}
+
+int launch_decode_stack(const lily_moe_dims& d, int n_layers, const lily_moe_weights* layers,
+                        const float* logits, const uint16_t* x0, float* r, uint16_t* outs,
+                        int32_t* topk_ids, float* topk_w, int32_t* sched, float eps,
+                        void* workspace, hipStream_t stream) {
+    StackArgs a{};
+    a.L = n_layers;
+    a.H = d.H;
+    a.F = d.F;
+    a.E = d.E;
+    a.k = d.topk;
+    a.layers = layers;
+    a.logits = logits;
+    a.x0 = x0;
+    a.r = r;
+    a.outs = outs;
+    a.topk_ids = topk_ids;
+    a.topk_w = topk_w;
+    a.h = static_cast<uint16_t*>(workspace);
+    a.rr = reinterpret_cast<float*>(static_cast<char*>(workspace) + stack_h_bytes(d));
+    a.eps = eps;
+    a.bar = sched + kDecodeBarrier;
+    a.grp = sched + kQueueInts;
+    a.err = sched + kDecodeBarrier + 2;
+    // At most one workgroup per compute unit, each needing a fraction of a
+    // compute unit's registers and LDS: all are resident at once, which the
+    // device-wide barriers rely on.
+    hipLaunchKernelGGL(moe_decode_stack_kernel, dim3((unsigned)decode_grid()), dim3(kDecThreads),
+                       0, stream, a);
+    return check_launch("decode_stack");
 }
 
 }  // namespace lily
