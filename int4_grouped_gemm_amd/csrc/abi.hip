@@ -364,7 +364,6 @@ int lily_moe_decode_stack(const lily_moe_dims* dims, int32_t n_layers,
                           void* stream) {
     int rc = check_dims(dims);
     if (rc) return rc;
-    if ((rc = decode_stack_supported(*dims, n_layers))) return rc;
     REQUIRE_PTR(layers);
     REQUIRE_PTR(logits);
     REQUIRE_PTR(x0);
@@ -374,6 +373,7 @@ int lily_moe_decode_stack(const lily_moe_dims* dims, int32_t n_layers,
     REQUIRE_PTR(topk_w);
     REQUIRE_PTR(sched);
     if (!(eps >= 0.0f)) return set_error(LILY_ERR_INVALID_ARG, "eps must be >= 0");
+    if ((rc = decode_stack_supported(*dims, n_layers))) return rc;
     if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
     return launch_decode_stack(*dims, n_layers, layers, logits, x0, r, outs, topk_ids, topk_w,
                                sched, eps, workspace, reinterpret_cast<hipStream_t>(stream));

@@ -122,6 +122,27 @@ def test_unfused_twin_rejects(lib):
     assert rc == L.LILY_ERR_INVALID_ARG and "down" in lib.lily_last_error().decode()
 
 
+def test_decode_stack_rejects(lib):
+    """lily_moe_decode_stack validates pointers, eps and sizes before any
+    device work."""
+    def call(d, n_layers=4, logits=FAKE, eps=1e-6):
+        return lib.lily_moe_decode_stack(ctypes.byref(d), n_layers, FAKE, logits, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, FAKE, ctypes.c_float(eps), FAKE, 1 << 40, None)
+    ok = good_dims(T=1, H=512, F=256)
+    assert call(ok, logits=None) == L.LILY_ERR_INVALID_ARG
+    assert "logits" in lib.lily_last_error().decode()
+    assert call(ok, eps=-1.0) == L.LILY_ERR_INVALID_ARG and "eps" in lib.lily_last_error().decode()
+    assert call(ok, n_layers=0) == L.LILY_ERR_INVALID_ARG
+    assert "n_layers" in lib.lily_last_error().decode()
+    assert call(good_dims(T=2, H=512, F=256)) == L.LILY_ERR_UNSUPPORTED
+    assert "T = 2" in lib.lily_last_error().decode()
+    assert call(good_dims(T=1, H=4096, F=256)) == L.LILY_ERR_UNSUPPORTED
+    assert "H = 4096" in lib.lily_last_error().decode()
+    assert call(good_dims(T=1, H=512, F=128)) == L.LILY_ERR_UNSUPPORTED
+    assert "F = 128" in lib.lily_last_error().decode()
+    assert call(ok, n_layers=2000) == L.LILY_ERR_UNSUPPORTED  # n_layers * topk beyond the LDS table
+
+
 def test_route_host_rejects(lib):
     """The host-synchronised twin validates like lily_moe_route, before any
     device work."""
