@@ -46,6 +46,11 @@ ROUTE_CASES = [
     ("E1_k1", 70, 1, 1, 16, None),
     ("E512_k64", 300, 512, 64, 64, None),
     ("odd_T", 777, 256, 8, 128, "prefill2048_zipf"),
+    # route_finish runs one workgroup per part of >= 128 tokens (at most 64 parts)
+    ("parts_T129_last_1", 129, 256, 8, 64, "prefill512"),
+    ("parts_T8192_64", 8192, 256, 8, 128, "prefill8192"),
+    ("parts_T8193_size129", 8193, 256, 8, 128, None),
+    ("parts_E512_k64", 1000, 512, 64, 64, None),
 ]
 
 
@@ -218,6 +223,20 @@ def test_forward_zipf2048_all_tokens(tile_m):
     # run-to-run determinism with a poisoned workspace
     again = G.from_dev_bits(G.forward_gpu(d, w, xd, r))
     assert np.array_equal(again, got), "forward is not deterministic"
+
+
+def test_forward_prefill8192_sampled():
+    """One T = 8192 layer call (64 route parts): routing bit-exact, and the
+    outputs of sampled tokens (part edges included) within the tolerance."""
+    cfg = S.CONFIGS["prefill8192"]
+    rng = np.random.default_rng(8192)
+    tokens = sorted(set([0, 1, 127, 128, 129, 4095, 4096, 8190, 8191] +
+                        rng.choice(cfg.T, 55, replace=False).tolist()))
+    _flush(f"forward prefill8192, {len(tokens)} sampled tokens")
+    got, acc, _ = _layer_case(cfg, 128, tokens=tokens)
+    err = G.output_error(got, acc)
+    _flush(f"  normalised error {err:.4f}")
+    assert err <= 1.0, f"normalised error {err}"
 
 
 # ------------------------------------------------------------------- packing
