@@ -11,8 +11,9 @@
 // and bias applied to each 32-weight dot product):
 //   phase 0  top-k and softmax of every token (each workgroup, redundantly);
 //   phase A  gate/up: unit = (row, 8 features): the 8 gate and 8 up weight
-//            rows of those features over all of K, one wavefront per unit,
-//            which forms h = bf16(silu(gate) * up) itself;
+//            rows of those features over all of K, split over the four
+//            wavefronts of a workgroup by K slices; their part sums meet in
+//            LDS and form h = bf16(silu(gate) * up);
 //   one device-wide barrier;
 //   phase B  down and combine: unit = (token, 8 output rows); the unit's
 //            W_down slices of the k + 1 rows times their h, weighted by the
@@ -33,6 +34,9 @@ constexpr int kDecodeMaxT = 4;       // lily_moe_decode serves T <= this
 constexpr int kDecMaxGrid = 512;     // workgroups: at most one per compute unit and this
 constexpr int kDecXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round robin over them
 constexpr int kDecASlices = 8;       // phase A slices per lane and weight matrix loaded at once
+constexpr int kDecMaxUnits = 16;     // lily_moe_decode: gate/up units per workgroup
+constexpr int kDecUnitBatch = 4;     // lily_moe_decode: units whose slices are loaded at once
+constexpr int kDecItBatch = 2;       // lily_moe_decode: slices per row and wavefront loaded at once
 constexpr int kDecBRounds = 6;       // phase B rounds per wavefront loaded at once
 constexpr int kDecLdsWords = 8192;   // LDS: x rows (phase A) or h rows (phase B), bf16 pairs
 constexpr int kDecXChunks = 8;       // x 16-byte chunks staged per thread: T * H <= 16384
@@ -219,6 +223,7 @@ __device__ __forceinline__ void barrier_exit(int32_t* bar, int32_t* grp, int lea
 __device__ __forceinline__ int range_begin(int w, int nb, int g) { return (unsigned)(w * nb) / (unsigned)g; }
 
 __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
+    __shared__ float s_pa[kDecMaxUnits][kDecThreads / kWave][16];  // phase A part sums
     __shared__ int32_t s_ids[kDecodeMaxT * kMaxTopk];
     __shared__ float s_w[kDecodeMaxT * kMaxTopk];
     __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDecLdsWords];
@@ -303,61 +308,97 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_kernel(DecodeArgs a) {
     };
 
     // Phase A: unit u = (row r, features f0 .. f0 + 7): the 8 gate rows and
-    // the 8 up rows of those features over all of K, one wavefront per unit;
-    // units are dealt to the workgroup with vw = u % G, then to its
-    // wavefronts in turn.
+    // the 8 up rows of those features over all of K. Units are dealt to the
+    // workgroup with vw = u % G; wavefront w takes the K slices i = w + 4 m
+    // of every unit of its workgroup, so the four wavefronts share each
+    // unit's dequantisation and dot products (one wavefront per unit left
+    // half of a compute unit's SIMDs idle in this VALU-heavy phase).
     // Lane l covers feature f0 + l % 8 and the 32-weight slices c = l / 8 +
     // 8 i of its rows (group c / 2, half c % 2): each load instruction reads
-    // whole 128-byte lines (8 rows x 16 bytes of one block half). The sums
-    // of the 8 lanes of a feature are added by shuffles, and lanes 0-7 form
-    // h = bf16(silu(gate) * up) themselves: no partial sums leave the
-    // wavefront.
+    // whole 128-byte lines (8 rows x 16 bytes of one block half). A
+    // wavefront's sums per unit (its 8 lanes of a feature added by shuffles)
+    // go to LDS; then threads add the four parts in wavefront order and form
+    // h = bf16(silu(gate) * up).
     const int UA = R * (F / 8);
     const int spr8 = H / 256;  // slices per lane per weight row
     const int l8 = lane % 8, lc = lane / 8;
-    for (int u = vw + G * wv; u < UA; u += 4 * G) {
-        const int r = u / (F / 8), f0 = (u - r * (F / 8)) * 8;
-        const int t = r / (k + 1), j = r - t * (k + 1);
-        const bool sh = (j == k);
-        const int e = sh ? 0 : s_ids[t * k + j];
-        const int s = f0 / kPackRows, rr = f0 % kPackRows + l8;
-        const size_t seg = ((size_t)e * nsf + s) * nkg * kPackBlock;
-        const Rsrc rg = make_rsrc((sh ? a.sh_gate : a.gate) + seg, nkg * kPackBlock);
-        const Rsrc ru = make_rsrc((sh ? a.sh_up : a.up) + seg, nkg * kPackBlock);
-        const int voff_q = (lc >> 1) * kPackBlock + ((lc & 1) * kPackRows + rr) * 16;
-        const int voff_s = (lc >> 1) * kPackBlock + kPackQ + rr * 2;
-        const int xbase = t * (H / 2) + (lc >> 1) * 32 + (lc & 1) * 16;
-        float ag = 0.0f, au = 0.0f;
-        for (int i0 = 0; i0 < spr8; i0 += kDecASlices) {
-            // slices past the row's end are clamped onto its last ones
-            // (loaded, not used)
-            Slice sg[kDecASlices], su[kDecASlices];
+    const int n_u = vw < UA ? (UA - vw + G - 1) / G : 0;  // <= kDecMaxUnits (host check)
+    const int n_it = (spr8 - wv + 3) / 4;                 // this wavefront's slices per row
+    const int qoff = (lc >> 1) * kPackBlock;
+    for (int ub = 0; ub < n_u; ub += kDecUnitBatch) {
+        float pg[kDecUnitBatch], pu[kDecUnitBatch];
+        Rsrc rg[kDecUnitBatch], ru[kDecUnitBatch];
+        int xb[kDecUnitBatch], rrs[kDecUnitBatch];
 #pragma unroll
-            for (int i = 0; i < kDecASlices; ++i) {
-                const int soff = min(i0 + i, spr8 - 1) * 4 * kPackBlock;
-                sg[i] = load_slice(rg, voff_q, voff_s, soff);
-                su[i] = load_slice(ru, voff_q, voff_s, soff);
-            }
+        for (int b = 0; b < kDecUnitBatch; ++b) {
+            pg[b] = pu[b] = 0.0f;
+            const int u = vw + G * min(ub + b, n_u - 1);  // past the end: a valid unit, unused
+            const int r = u / (F / 8), f0 = (u - r * (F / 8)) * 8;
+            const int t = r / (k + 1), j = r - t * (k + 1);
+            const bool sh = (j == k);
+            const int e = sh ? 0 : s_ids[t * k + j];
+            const size_t seg = ((size_t)e * nsf + f0 / kPackRows) * nkg * kPackBlock;
+            rg[b] = make_rsrc((sh ? a.sh_gate : a.gate) + seg, nkg * kPackBlock);
+            ru[b] = make_rsrc((sh ? a.sh_up : a.up) + seg, nkg * kPackBlock);
+            rrs[b] = f0 % kPackRows + l8;
+            xb[b] = t * (H / 2) + (lc >> 1) * 32 + (lc & 1) * 16;
+        }
+        for (int m0 = 0; m0 < n_it; m0 += kDecItBatch) {
+            Slice sg[kDecUnitBatch][kDecItBatch], su[kDecUnitBatch][kDecItBatch];
 #pragma unroll
-            for (int i = 0; i < kDecASlices; ++i) {
-                if (i0 + i < spr8) {
-                    const int xo = xbase + (i0 + i) * 128;
-                    ag += dot_slice(sg[i], s_buf + xo);
-                    au += dot_slice(su[i], s_buf + xo);
+            for (int b = 0; b < kDecUnitBatch; ++b)
+#pragma unroll
+                for (int m = 0; m < kDecItBatch; ++m) {
+                    // slices past the row's end are clamped onto its last one
+                    const int soff = min(wv + 4 * (m0 + m), spr8 - 1) * 4 * kPackBlock;
+                    const int vq = qoff + ((lc & 1) * kPackRows + rrs[b]) * 16;
+                    const int vs = qoff + kPackQ + rrs[b] * 2;
+                    sg[b][m] = load_slice(rg[b], vq, vs, soff);
+                    su[b][m] = load_slice(ru[b], vq, vs, soff);
                 }
+#pragma unroll
+            for (int b = 0; b < kDecUnitBatch; ++b)
+#pragma unroll
+                for (int m = 0; m < kDecItBatch; ++m)
+                    if (ub + b < n_u && m0 + m < n_it) {
+                        const int xo = xb[b] + (wv + 4 * (m0 + m)) * 128;
+                        pg[b] += dot_slice(sg[b][m], s_buf + xo);
+                        pu[b] += dot_slice(su[b][m], s_buf + xo);
+                    }
+        }
+#pragma unroll
+        for (int b = 0; b < kDecUnitBatch; ++b) {
+            pg[b] += __shfl_xor(pg[b], 8);
+            pg[b] += __shfl_xor(pg[b], 16);
+            pg[b] += __shfl_xor(pg[b], 32);
+            pu[b] += __shfl_xor(pu[b], 8);
+            pu[b] += __shfl_xor(pu[b], 16);
+            pu[b] += __shfl_xor(pu[b], 32);
+            if (lane < 8 && ub + b < n_u) {
+                s_pa[ub + b][wv][lane] = pg[b];
+                s_pa[ub + b][wv][8 + lane] = pu[b];
             }
         }
-        ag += __shfl_xor(ag, 8);
-        ag += __shfl_xor(ag, 16);
-        ag += __shfl_xor(ag, 32);
-        au += __shfl_xor(au, 8);
-        au += __shfl_xor(au, 16);
-        au += __shfl_xor(au, 32);
-        const float hv = silu(ag) * au;
-        const float hn = __shfl_down(hv, 1);
-        if (lane < 8 && (lane & 1) == 0)
-            __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h + (size_t)r * F + f0 + lane),
-                               pack_bf16x2(hv, hn), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_barrier();
+    // thread (unit ui, pair q): features 2q, 2q + 1 of the unit
+    if (tid < 4 * n_u) {
+        const int ui = tid / 4, q = tid % 4;
+        const int u = vw + G * ui;
+        const int r = u / (F / 8), f0 = (u - r * (F / 8)) * 8;
+        float hv[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float g = 0.0f, up = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kDecThreads / kWave; ++w) {
+                g += s_pa[ui][w][2 * q + c];
+                up += s_pa[ui][w][8 + 2 * q + c];
+            }
+            hv[c] = silu(g) * up;
+        }
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h + (size_t)r * F + f0 + 2 * q),
+                           pack_bf16x2(hv[0], hv[1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // Phase B's first rounds are loaded once this workgroup has counted in
     // at the barrier, so that they do not compete with phase A's loads; they
@@ -823,6 +864,12 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
     a.err = r.sched + kDecodeBarrier + 2;
     static_assert(kQueueInts + kBarGroups * kBarLine <= kSchedInts, "barrier group counters");
     const int g = decode_grid();
+    // (checked here, after the arguments: it depends on the device)
+    const long units = (long)d.T * (d.topk + 1) * (d.F / 8);
+    if (units > (long)kDecMaxUnits * g)
+        return set_error(LILY_ERR_UNSUPPORTED,
+                         "T * (topk + 1) * F / 8 = %ld gate/up units exceed %d per compute unit",
+                         units, kDecMaxUnits);
     // At most one workgroup per compute unit, each needing a fraction of a
     // compute unit's registers and LDS: all are resident at once, which the
     // device-wide barrier relies on.
