@@ -508,6 +508,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_stack_kernel(StackArgs
     __shared__ float s_bred[kDecThreads / kWave][kDecPiece];
     __shared__ float s_part[kDecThreads / kWave];
     __shared__ float s_r[kDecASlices * 256];  // r_l (H <= 2048)
+    __shared__ float s_pa[kDecUnitBatch][kDecThreads / kWave][16];  // phase A part sums
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -525,20 +526,19 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_stack_kernel(StackArgs
     const int R = k + 1;
     const int nkg = H / kGroup, nsf = F / kPackRows, nkgF = F / kGroup, nsH = H / kPackRows;
 
-    // Phase A unit of this wavefront (at most one: the host checks
-    // R * F / 8 <= 4 G): unit u = (row j, features f0 .. f0 + 7).
-    const int u = vw + G * wv;
-    const bool has_unit = u < R * (F / 8);
-    const int uj = has_unit ? u / (F / 8) : 0;
-    const int f0 = has_unit ? (u - uj * (F / 8)) * 8 : 0;
-    const bool ush = uj == k;
+    // Phase A units of this workgroup (at most kDecUnitBatch: the host
+    // checks R * F / 8 <= 4 G): unit u = (row j, features f0 .. f0 + 7) for
+    // u = vw + G i. As in moe_decode_kernel, wavefront w takes the K slices
+    // w, w + 4, ... of each of them (at most kDecItBatch: H <= 2048), and the
+    // part sums meet in LDS.
+    const int UA = R * (F / 8);
+    const int n_u = vw < UA ? (UA - vw + G - 1) / G : 0;
     const int l8 = lane % 8, lc = lane / 8;
-    const int spr8 = H / 256;  // <= kDecASlices (host check)
-    const int rr = f0 % kPackRows + l8;
-    const int voff_q = (lc >> 1) * kPackBlock + ((lc & 1) * kPackRows + rr) * 16;
-    const int voff_s = (lc >> 1) * kPackBlock + kPackQ + rr * 2;
+    const int spr8 = H / 256;
+    const int n_it = (spr8 - wv + 3) / 4;
+    const int qoff = (lc >> 1) * kPackBlock;
     const int xbase = (lc >> 1) * 32 + (lc & 1) * 16;
-    Slice sg[kDecASlices], su[kDecASlices];
+    Slice sg[kDecUnitBatch][kDecItBatch], su[kDecUnitBatch][kDecItBatch];
 
     // Phase B unit range (output rows of 8).
     const int UB = H / kDecPiece;
@@ -560,21 +560,31 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_stack_kernel(StackArgs
             a.topk_ids[i] = s_ids[i];
             a.topk_w[i] = s_w[i];
         }
-    // Gate/up weight loads of this wavefront's unit for layer l.
+    // Gate/up weight loads of this wavefront's slices for layer l (units and
+    // slices past the end are clamped onto valid ones: loaded, not used).
     auto issue_a = [&](int l) {
-        if (!has_unit) return;
+        if (n_u == 0) return;
         const lily_moe_weights& w = a.layers[l];
-        const int e = ush ? 0 : s_ids[l * k + uj];
-        const size_t seg = ((size_t)e * nsf + f0 / kPackRows) * nkg * kPackBlock;
-        const Rsrc rg = make_rsrc(static_cast<const char*>(ush ? w.sh_gate : w.gate) + seg,
-                                  nkg * kPackBlock);
-        const Rsrc ru = make_rsrc(static_cast<const char*>(ush ? w.sh_up : w.up) + seg,
-                                  nkg * kPackBlock);
 #pragma unroll
-        for (int i = 0; i < kDecASlices; ++i) {
-            const int soff = min(i, spr8 - 1) * 4 * kPackBlock;
-            sg[i] = load_slice(rg, voff_q, voff_s, soff);
-            su[i] = load_slice(ru, voff_q, voff_s, soff);
+        for (int b = 0; b < kDecUnitBatch; ++b) {
+            const int u = vw + G * min(b, n_u - 1);
+            const int j = u / (F / 8), f0 = (u - j * (F / 8)) * 8;
+            const bool sh = j == k;
+            const int e = sh ? 0 : s_ids[l * k + j];
+            const size_t seg = ((size_t)e * nsf + f0 / kPackRows) * nkg * kPackBlock;
+            const Rsrc rg = make_rsrc(static_cast<const char*>(sh ? w.sh_gate : w.gate) + seg,
+                                      nkg * kPackBlock);
+            const Rsrc ru = make_rsrc(static_cast<const char*>(sh ? w.sh_up : w.up) + seg,
+                                      nkg * kPackBlock);
+            const int rr = f0 % kPackRows + l8;
+            const int vq = qoff + ((lc & 1) * kPackRows + rr) * 16;
+            const int vs = qoff + kPackQ + rr * 2;
+#pragma unroll
+            for (int m = 0; m < kDecItBatch; ++m) {
+                const int soff = min(wv + 4 * m, spr8 - 1) * 4 * kPackBlock;
+                sg[b][m] = load_slice(rg, vq, vs, soff);
+                su[b][m] = load_slice(ru, vq, vs, soff);
+            }
         }
     };
     // One phase B round: slot j = rho / nq, groups 4 gq .. 4 gq + 3 of unit ub.
@@ -597,9 +607,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_stack_kernel(StackArgs
     const int ub_first = ub0 < ub1 ? ub0 : 0;
 
     // The last wavefront loads r and h for the workgroup, stores each
-    // layer's out and r, counts the workgroup in and polls: it holds no
-    // gate/up unit when units fill at most three wavefronts per workgroup,
-    // so none of its loads queues behind gate/up loads.
+    // layer's out and r, counts the workgroup in and polls.
     constexpr int kLeadWave = kDecThreads / kWave - 1;
     constexpr int kLead = kLeadWave * kWave;
     int inst = 0;  // barrier instances passed or arrived at
@@ -683,33 +691,50 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_stack_kernel(StackArgs
 #pragma unroll
         for (int n = 0; n < kDecBRounds; ++n)
             pb[n] = b_round(l, ub_first, min(wv + 4 * n, NRB - 1), pw[n], ph[n]);
-        // Phase A of layer l: the unit's loads were issued earlier.
-        if (has_unit) {
-            float ag = 0.0f, au = 0.0f;
+        // Phase A of layer l: the slices' loads were issued earlier.
 #pragma unroll
-            for (int i = 0; i < kDecASlices; ++i) {
-                if (i < spr8) {
-                    const int xo = xbase + i * 128;
-                    ag += dot_slice(sg[i], s_buf + xo);
-                    au += dot_slice(su[i], s_buf + xo);
+        for (int b = 0; b < kDecUnitBatch; ++b) {
+            float pg = 0.0f, pu = 0.0f;
+#pragma unroll
+            for (int m = 0; m < kDecItBatch; ++m)
+                if (b < n_u && m < n_it) {
+                    const int xo = xbase + (wv + 4 * m) * 128;
+                    pg += dot_slice(sg[b][m], s_buf + xo);
+                    pu += dot_slice(su[b][m], s_buf + xo);
                 }
+            pg += __shfl_xor(pg, 8);
+            pg += __shfl_xor(pg, 16);
+            pg += __shfl_xor(pg, 32);
+            pu += __shfl_xor(pu, 8);
+            pu += __shfl_xor(pu, 16);
+            pu += __shfl_xor(pu, 32);
+            if (lane < 8 && b < n_u) {
+                s_pa[b][wv][lane] = pg;
+                s_pa[b][wv][8 + lane] = pu;
             }
-            ag += __shfl_xor(ag, 8);
-            ag += __shfl_xor(ag, 16);
-            ag += __shfl_xor(ag, 32);
-            au += __shfl_xor(au, 8);
-            au += __shfl_xor(au, 16);
-            au += __shfl_xor(au, 32);
-            const float hv = silu(ag) * au;
-            const float hn = __shfl_down(hv, 1);
-            if (lane < 8 && (lane & 1) == 0) {
-                const uint32_t hw = pack_bf16x2(hv, hn);
+        }
+        lds_barrier();
+        if (tid < 4 * n_u) {  // thread (unit ui, pair q): features 2q, 2q + 1
+            const int ui = tid / 4, q = tid % 4;
+            const int u = vw + G * ui;
+            const int j = u / (F / 8), f0 = (u - j * (F / 8)) * 8;
+            float hv[2];
 #pragma unroll
-                for (int c = 0; c < kDecXcds; ++c)
-                    __hip_atomic_store(
-                        reinterpret_cast<uint32_t*>(a.h + ((size_t)c * R + uj) * F + f0 + lane), hw,
-                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int c = 0; c < 2; ++c) {
+                float g = 0.0f, up = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kDecThreads / kWave; ++w) {
+                    g += s_pa[ui][w][2 * q + c];
+                    up += s_pa[ui][w][8 + 2 * q + c];
+                }
+                hv[c] = silu(g) * up;
             }
+            const uint32_t hw = pack_bf16x2(hv[0], hv[1]);
+#pragma unroll
+            for (int c = 0; c < kDecXcds; ++c)
+                __hip_atomic_store(
+                    reinterpret_cast<uint32_t*>(a.h + ((size_t)c * R + j) * F + f0 + 2 * q), hw,
+                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         barrier_arrive(a.bar, a.grp, kLead, true);
         const int inst_h = inst++;
