@@ -799,11 +799,7 @@ __global__ void __launch_bounds__(kDecThreads) moe_decode_stack_kernel(StackArgs
                 const int n = ub * kDecPiece + tid - kLead;
                 const uint16_t ob = float_to_bf16_bits(o);
                 a.outs[(size_t)l * H + n] = ob;
-                const float rprev = l == 0 ? bf16_bits_to_float(a.x0[n])
-                                           : __hip_atomic_load(a.rr + (size_t)xc * H + n,
-                                                               __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT);
-                const float rn = rprev + bf16_bits_to_float(ob);
+                const float rn = s_r[n] + bf16_bits_to_float(ob);  // r_l, staged for the norm
 #pragma unroll
                 for (int c = 0; c < kDecXcds; ++c)
                     __hip_atomic_store(a.rr + (size_t)c * H + n, rn, __ATOMIC_RELAXED,
