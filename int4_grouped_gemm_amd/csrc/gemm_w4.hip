@@ -20,11 +20,12 @@
 // group, with their scales and biases, are one contiguous 4608-byte block.
 //
 // The grid is persistent (as many workgroups as fit on the device) and
-// takes tiles from eight work queues, one per XCD: queue x owns the blocks
-// x, x + 8, ... of the schedule (the shared expert's blocks, then the
-// routed blocks in block_order, largest first, read resolved from
-// block_info), with their n-tiles consecutive so that they meet the same A
-// rows in one L2.
+// takes tiles from eight work queues, one per XCD. The schedule (the shared
+// expert's blocks, then the routed blocks in block_order, largest first,
+// read resolved from block_info) is dealt to the queues in turns of
+// kQueueChunk consecutive blocks, so that most blocks of a hot expert meet
+// its weight slabs in one XCD's L2; a block's n-tiles are consecutive, so
+// that they meet the same A rows there too.
 //
 // LDS A tiles are [rows][64] bf16 with the 16-byte chunks of each row
 // XOR-swizzled by ((row >> 1) & 7). The LDS has 64 four-byte banks, so a
@@ -85,6 +86,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 // is the 16-byte chunk 4h + s of its row.
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
+constexpr int kQueueChunk = 4;  // consecutive schedule blocks per queue turn
 
 template <bool GATED>
 struct GemmShape {
@@ -491,10 +493,15 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
     const int cq = blockIdx.x % kXcds;
     int toggle = 0;
 
-    // Items of queue q: its blocks q, q + 8, ... times the n-tiles times the
-    // K chunks (the chunks of a tile consecutive).
+    // Items of queue q: its blocks times the n-tiles times the K chunks (the
+    // chunks of a tile consecutive). Queue q owns the schedule's chunks of
+    // kQueueChunk blocks q, q + 8, ...; the last chunk may be short.
     auto items_of = [&](int q) {
-        return (nb_total > q ? (nb_total - q + kXcds - 1) / kXcds : 0) * n_tiles * args.kc;
+        if (nb_total == 0) return 0;
+        const int kl = (nb_total - 1) / kQueueChunk;  // last chunk
+        const int nch = kl >= q ? (kl - q) / kXcds + 1 : 0;
+        const int nb = nch * kQueueChunk - (kl % kXcds == q ? (kl + 1) * kQueueChunk - nb_total : 0);
+        return nb * n_tiles * args.kc;
     };
     // Takes the next item of queue cq (one atomic) and resolves its rows,
     // expert and load plan (one load of block_info); it.valid = false if the
@@ -506,7 +513,8 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
         {
             const int ct = c / args.kc;  // tile of the queue
             it.chunk = c - ct * args.kc;
-            const int vb = cq + kXcds * (ct / n_tiles);
+            const int qi = ct / n_tiles;  // block of the queue
+            const int vb = ((qi / kQueueChunk) * kXcds + cq) * kQueueChunk + qi % kQueueChunk;
             const int nt = ct % n_tiles;
             it.tile = vb * n_tiles + nt;
             int e = 0;
