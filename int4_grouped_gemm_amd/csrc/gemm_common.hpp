@@ -1,0 +1,103 @@
+// Pieces shared by the two grouped-GEMM kernels (gfx950): the kernel
+// arguments, the schedule of work items over the XCD queues, the LDS swizzle,
+// hand-counted memory waits and the global -> LDS DMA instructions.
+#pragma once
+
+#include "common.hpp"
+#include "w4.hpp"
+
+namespace lily {
+
+struct GemmArgs {
+    const uint16_t* a;              // A rows: gate/up -> x [T, K]; down -> h [P + T, K]
+    const int32_t* sorted_pairs;    // gate/up: routed row r reads x[sorted_pairs[r] / topk]
+    int topk;
+    const char* w[2];               // packed routed stacks: gate/up -> gate, up; down -> W_down twice
+    const char* sw[2];              // packed shared-expert stacks, same roles
+    int N, K;
+    const int4* block_info;         // per schedule position: expert, first row, rows, block
+    const int32_t* num_blocks;
+    int shared_blocks;  // ceil(T / BM)
+    int P, T;
+    int32_t* sched;     // kXcds queue counters, then the finished-workgroup counter
+    uint16_t* h_out;    // gate/up: h [P + T, N] bf16
+    float* y_out;       // down: y [P + T, N] fp32
+    // Split K (small block maps): each tile's K runs as kc items of K / kc;
+    // their fp32 partial sums go to part [kc][P + T][NP] (NP = 2N for
+    // gate/up: g then u; N for down) and the item that finishes a tile, as
+    // counted in tile_ctr [tiles], sums them in chunk order.
+    int kc;
+    float* part;
+    int32_t* tile_ctr;
+};
+
+constexpr int kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own L2
+constexpr int kQueueChunk = 4;  // consecutive schedule blocks per queue turn
+
+// Output columns of one work item: the gate/up GEMM takes 128 features
+// (128 gate and the same 128 up weight rows, so that SwiGLU is local to a
+// lane), the down GEMM 256 rows of W_down. Either way two packed slabs.
+template <bool GATED>
+struct GemmShape {
+    static constexpr int BN = GATED ? 128 : 256;
+};
+
+// The schedule (the shared expert's blocks, then the routed blocks in
+// block_order) is dealt to kXcds queues in turns of kQueueChunk consecutive
+// blocks: queue q owns blocks q*c .. q*c + c-1, (q + 8)*c .., ... (c =
+// kQueueChunk), so that most blocks of a hot expert meet its weight slabs
+// in one XCD's L2. Each block contributes n_tiles * kc consecutive items.
+__device__ __forceinline__ int queue_items(int nb_total, int q, int per_block) {
+    if (nb_total == 0) return 0;
+    const int kl = (nb_total - 1) / kQueueChunk;  // last chunk
+    const int nch = kl >= q ? (kl - q) / kXcds + 1 : 0;
+    const int nb = nch * kQueueChunk - (kl % kXcds == q ? (kl + 1) * kQueueChunk - nb_total : 0);
+    return nb * per_block;
+}
+// Schedule position of the qi-th block of queue q.
+__device__ __forceinline__ int queue_block(int q, int qi) {
+    return ((qi / kQueueChunk) * kXcds + q) * kQueueChunk + qi % kQueueChunk;
+}
+
+// LDS tiles of 64 bf16 per row ([rows][64]) store the 16-byte chunks of a
+// row XOR-swizzled by ((row >> 1) & 7). The LDS has 64 four-byte banks, so a
+// 16-lane phase of a 16-byte access covers 256 bytes: rows r and r + 1 of
+// one chunk column already fall in different halves of the banks, and the
+// swizzle spreads each half's eight rows over its eight chunk slots.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+// Workgroup barrier without the memory fences of __syncthreads (which would
+// drain every load in flight); the empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Global -> LDS load (gfx950 LDS DMA) with a wave-uniform 64-bit base in
+// SGPRs and a 32-bit per-lane byte offset; lane l lands at LDS address
+// m0 + l * size. The loads count in vmcnt like any vector memory load, but
+// the compiler does not see them: their waits are counted by hand.
+__device__ __forceinline__ void dma16(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
+                    "s"(uniform_ptr(base)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
+                    "s"(uniform_ptr(base)) : "memory");
+}
+
+}  // namespace lily

@@ -27,42 +27,12 @@
 // its weight slabs in one XCD's L2; a block's n-tiles are consecutive, so
 // that they meet the same A rows there too.
 //
-// LDS A tiles are [rows][64] bf16 with the 16-byte chunks of each row
-// XOR-swizzled by ((row >> 1) & 7). The LDS has 64 four-byte banks, so a
-// 16-lane phase of a 16-byte read covers 256 bytes: rows r and r + 1 of one
-// chunk column already fall in different halves of the banks, and the
-// swizzle spreads each half's eight rows over its eight chunk slots.
+// LDS A tiles are [rows][64] bf16 with the chunk swizzle of gemm_common.hpp.
 #include <algorithm>
 
-#include "common.hpp"
-#include "w4.hpp"
+#include "gemm_common.hpp"
 
 namespace lily {
-
-struct GemmArgs {
-    const uint16_t* a;              // A rows: gate/up -> x [T, K]; down -> h [P + T, K]
-    const int32_t* sorted_pairs;    // gate/up: routed row r reads x[sorted_pairs[r] / topk]
-    int topk;
-    const char* w[2];               // packed routed stacks: gate/up -> gate, up; down -> W_down twice
-    const char* sw[2];              // packed shared-expert stacks, same roles
-    int N, K;
-    const int4* block_info;         // per schedule position: expert, first row, rows, block
-    const int32_t* num_blocks;
-    int shared_blocks;  // ceil(T / BM)
-    int P, T;
-    int32_t* sched;     // kXcds queue counters, then the finished-workgroup counter
-    uint16_t* h_out;    // gate/up: h [P + T, N] bf16
-    float* y_out;       // down: y [P + T, N] fp32
-    // Split K (small block maps): each tile's K runs as kc items of K / kc;
-    // their fp32 partial sums go to part [kc][P + T][NP] (NP = 2N for
-    // gate/up: g then u; N for down) and the item that finishes a tile, as
-    // counted in tile_ctr [tiles], sums them in chunk order.
-    int kc;
-    float* part;
-    int32_t* tile_ctr;
-};
-
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // Tile geometry. A workgroup has 4 wavefronts that split the output columns;
 // every wavefront covers all BM rows of the block. The workgroup owns 256
@@ -85,13 +55,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 // 8s..8s+7 of each half, for A and B alike. So a lane's A operand for step s
 // is the 16-byte chunk 4h + s of its row.
 constexpr int kGemmThreads = 256;
-constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
-constexpr int kQueueChunk = 4;  // consecutive schedule blocks per queue turn
-
-template <bool GATED>
-struct GemmShape {
-    static constexpr int BN = GATED ? 128 : 256;  // output columns per workgroup
-};
 
 // Per tile height: k-steps in flight through LDS and wavefronts per SIMD.
 // A single wavefront issues a VALU instruction only every few cycles, so the
@@ -125,39 +88,6 @@ struct Lds {
     static_assert(A_OFF + (NS - 1) * A < 65536 && Q_OFF + (NS - 1) * Q < 65536,
                   "stage bases must fit ds_read offsets");
 };
-
-// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() {
-    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
-}
-// Workgroup barrier without the memory fences of __syncthreads (which would
-// drain every load in flight); the empty asm statements keep the compiler
-// from moving memory accesses across it.
-__device__ __forceinline__ void barrier_only() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Global -> LDS load (gfx950 LDS DMA) with a wave-uniform 64-bit base in
-// SGPRs and a 32-bit per-lane byte offset; lane l lands at LDS address
-// m0 + l * size. The kernel's own code uses M0 for nothing else.
-__device__ __forceinline__ void dma16(const void* base, uint32_t lane_off, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
-                    "s"(uniform_ptr(base)) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t lane_off, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-                 :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
-                    "s"(uniform_ptr(base)) : "memory");
-}
 
 // Next item of a work queue, the same value in every thread of the
 // workgroup. Consecutive calls alternate between two LDS slots, so a slot is
@@ -301,7 +231,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
                 for (int i = 0; i < MIA; ++i)
 #pragma unroll
                     for (int g = 0; g < NI; ++g)
-                        acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[g], acc[i][g], 0, 0, 0);
+                        acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[g], af[i], acc[i][g], 0, 0, 0);
             }
             wait_lgkmcnt0();
             return;
@@ -348,7 +278,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
             for (int i = 0; i < MIA; ++i)
 #pragma unroll
                 for (int g = 0; g < NI; ++g)
-                    acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][g], acc[i][g], 0, 0, 0);
+                    acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][g], af[s & 1][i], acc[i][g], 0, 0, 0);
         }
         // Issue order for the scheduler: the weights' reads and sub-step 0's
         // A reads, the scale/bias conversion and sub-step 0's dequantisation;
@@ -389,8 +319,11 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
 
     prep_next();
 
-    // C layout of a 32x32 tile: lane l, register r holds row
-    // 8*(r/4) + 4*(l/32) + r%4 and column l%32.
+    // The MFMAs take the weights as their first operand and the A rows as the
+    // second, so lane l, register r of tile (i, g) holds output row
+    // 32 i + l % 32 and column col0[g] + 8 (r / 4) + 4 (l / 32) + r % 4: four
+    // consecutive columns per group of four registers, stored together.
+    const int x = lane % 32;
     if (args.kc > 1) {
         // Split K: publish this chunk's partial sums; the item that
         // completes the tile (the kc-th to arrive at its counter) adds all
@@ -399,18 +332,17 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         const int np = GATED ? 2 * args.N : args.N;
         const size_t chunk_stride = (size_t)(args.P + args.T) * np;
 #pragma unroll
-        for (int i = 0; i < MIA; ++i)
+        for (int i = 0; i < MIA; ++i) {
+            const int row = 32 * i + x;
+            if (row >= rows) continue;
+            float* prow = args.part + lp.chunk * chunk_stride + (size_t)(r0 + row) * np;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-                if (row < rows) {
-                    float* prow = args.part + lp.chunk * chunk_stride + (size_t)(r0 + row) * np;
+            for (int g = 0; g < NI; ++g)
 #pragma unroll
-                    for (int g = 0; g < NI; ++g)
-                        __hip_atomic_store(prow + (GATED ? g * args.N + col0[0] : col0[g]) + lane % 32,
-                                           acc[i][g][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
+                for (int r = 0; r < 16; ++r)
+                    __hip_atomic_store(prow + (GATED ? g * args.N + col0[0] : col0[g]) + 8 * (r / 4) + 4 * h + r % 4,
+                                       acc[i][g][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         // The partials are device-coherent stores (they write through the
         // XCD's L2). Every wavefront waits for its own stores to complete
         // before the barrier (a workgroup barrier alone does not wait for
@@ -425,43 +357,46 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(*s_flag) != args.kc - 1) return;
 #pragma unroll
-        for (int i = 0; i < MIA; ++i)
+        for (int i = 0; i < MIA; ++i) {
+            const int row = 32 * i + x;
+            if (row >= rows) continue;
+            const float* prow = args.part + (size_t)(r0 + row) * np;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-                if (row < rows) {
-                    const float* prow = args.part + (size_t)(r0 + row) * np;
+            for (int g = 0; g < NI; ++g)
 #pragma unroll
-                    for (int g = 0; g < NI; ++g) {
-                        const int col = (GATED ? g * args.N + col0[0] : col0[g]) + lane % 32;
-                        float sum = 0.0f;
-                        for (int c = 0; c < args.kc; ++c)
-                            sum += __hip_atomic_load(prow + c * chunk_stride + col, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                        acc[i][g][r] = sum;
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int col = (GATED ? g * args.N + col0[0] : col0[g]) + 8 * (r / 4) + 4 * h + r % 4;
+                    float sum = 0.0f;
+                    for (int c = 0; c < args.kc; ++c)
+                        sum += __hip_atomic_load(prow + c * chunk_stride + col, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                    acc[i][g][r] = sum;
                 }
-            }
+        }
         if (threadIdx.x == 0)
             __hip_atomic_store(args.tile_ctr + lp.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Epilogue.
+    // Epilogue: 8 bytes of h (four bf16) or 16 bytes of y per store.
 #pragma unroll
     for (int i = 0; i < MIA; ++i) {
+        const int row = 32 * i + x;
+        if (row >= rows) continue;
+        const size_t orow = (size_t)(r0 + row) * args.N;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-            if (row < rows) {
-                const size_t orow = (size_t)(r0 + row) * args.N;
-                if (GATED) {
-                    const float g = acc[i][0][r];
-                    const float u = acc[i][1][r];
-                    args.h_out[orow + col0[0] + lane % 32] = float_to_bf16_bits(silu(g) * u);
-                } else {
+        for (int q = 0; q < 4; ++q) {
+            if (GATED) {
+                float v[4];
 #pragma unroll
-                    for (int g = 0; g < NI; ++g) args.y_out[orow + col0[g] + lane % 32] = acc[i][g][r];
-                }
+                for (int j = 0; j < 4; ++j) v[j] = silu(acc[i][0][4 * q + j]) * acc[i][1][4 * q + j];
+                *reinterpret_cast<u32x2*>(args.h_out + orow + col0[0] + 8 * q + 4 * h) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            } else {
+#pragma unroll
+                for (int g = 0; g < NI; ++g)
+                    *reinterpret_cast<f32x4*>(args.y_out + orow + col0[g] + 8 * q + 4 * h) =
+                        f32x4{acc[i][g][4 * q], acc[i][g][4 * q + 1], acc[i][g][4 * q + 2],
+                              acc[i][g][4 * q + 3]};
             }
         }
     }
@@ -496,13 +431,7 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
     // Items of queue q: its blocks times the n-tiles times the K chunks (the
     // chunks of a tile consecutive). Queue q owns the schedule's chunks of
     // kQueueChunk blocks q, q + 8, ...; the last chunk may be short.
-    auto items_of = [&](int q) {
-        if (nb_total == 0) return 0;
-        const int kl = (nb_total - 1) / kQueueChunk;  // last chunk
-        const int nch = kl >= q ? (kl - q) / kXcds + 1 : 0;
-        const int nb = nch * kQueueChunk - (kl % kXcds == q ? (kl + 1) * kQueueChunk - nb_total : 0);
-        return nb * n_tiles * args.kc;
-    };
+    auto items_of = [&](int q) { return queue_items(nb_total, q, n_tiles * args.kc); };
     // Takes the next item of queue cq (one atomic) and resolves its rows,
     // expert and load plan (one load of block_info); it.valid = false if the
     // queue is empty.
@@ -514,7 +443,7 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
             const int ct = c / args.kc;  // tile of the queue
             it.chunk = c - ct * args.kc;
             const int qi = ct / n_tiles;  // block of the queue
-            const int vb = ((qi / kQueueChunk) * kXcds + cq) * kQueueChunk + qi % kQueueChunk;
+            const int vb = queue_block(cq, qi);
             const int nt = ct % n_tiles;
             it.tile = vb * n_tiles + nt;
             int e = 0;
