@@ -15,6 +15,14 @@ step), timed with the wall clock between two device synchronisations.
 per launch over its average duration from HIP events recorded on the launch
 stream around every launch in the timed region. ``cpu_baseline`` times the
 CPU oracle on a bounded sample of the same workload.
+
+By default the run also measures the other configurations of the layer at
+their stated sizes and reports them as extra keys (``extra``): one layer at
+T = 512 (uniform routing, weight-streaming), and batch-1 decode through 40
+distinct resident layers in one launch per step. ``--peaks`` measures the
+device's achievable MFMA and HBM-read peaks instead (the calibration kernels
+of include/lily_calib.h) and writes them to profiles/peaks.json, from which
+``roofline.frac_of_measured`` is reported.
 """
 from __future__ import annotations
 
@@ -33,13 +41,15 @@ WORKLOAD = "prefill2048_zipf"
 PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill2048_zipf.txt")
+PEAKS_FILE = os.path.join(ROOT, "profiles", "peaks.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "int4_grouped_gemm_amd", "csrc", f)
-                  for f in ("gemm_w4.hip", "route.hip", "common.hpp", "topk.hpp", "w4.hpp")]
+                  for f in ("gemm_w4.hip", "gemm_common.hpp", "route.hip", "common.hpp", "topk.hpp",
+                            "w4.hpp")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -53,12 +63,14 @@ def parse():
                          "stack40 (40 distinct layers, T=8192 in chunks of 2048, residual glue)")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layers", type=int, default=8, help="distinct layer weight sets cycled")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="distinct layer weight sets (prefill: cycled, default 8; decode: "
+                         "default 40, the stack's own depth)")
     ap.add_argument("--tile-m", type=int, default=128)
-    ap.add_argument("--decode-path", default="fused", choices=["fused", "layer", "stack"],
-                    help="decode40: lily_moe_decode (one launch per layer), route + forward, or "
-                         "lily_moe_decode_stack (the 40 layers and their residual glue in one "
-                         "launch)")
+    ap.add_argument("--decode-path", default="stack", choices=["fused", "layer", "stack"],
+                    help="decode40: lily_moe_decode_stack (the 40 layers and their residual "
+                         "glue in one launch), lily_moe_decode (one launch per layer), or "
+                         "route + forward")
     ap.add_argument("--router", action="store_true",
                     help="start each step from x: the router projection x.Wr^T (lily_moe_router) "
                          "computes the logits inside the timed step")
@@ -70,11 +82,17 @@ def parse():
                          "then lily_moe_forward_bf16 (the same GEMMs on bf16 tiles); tile_m 32 "
                          "or 64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline only: skip the T=512 and decode40 measurements")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of layer 0 the CPU oracle computes for the baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 256 MiB device copy (twice) so that "
                          "profiler byte counters can be scaled against a known size")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the achievable MFMA and HBM-read peaks and the clock; with "
+                         "--write-peaks, record them in profiles/peaks.json")
+    ap.add_argument("--write-peaks", action="store_true")
     return ap.parse_args()
 
 
@@ -95,18 +113,64 @@ def stage_work(cfg, P):
     }
 
 
+def expert_bytes(cfg) -> float:
+    """Packed bytes of one expert's three matrices (4.5 bits per weight)."""
+    return 3 * cfg.H * cfg.F * (0.5 + 4.0 / 64)
+
+
+def measured_peaks():
+    """The achievable peaks recorded by --peaks, or None."""
+    if not os.path.exists(PEAKS_FILE):
+        return None
+    try:
+        return json.load(open(PEAKS_FILE))
+    except (OSError, ValueError):
+        return None
+
+
+def frac_of_measured(bound, achieved):
+    pk = measured_peaks()
+    if not pk:
+        return None
+    ref = pk.get("mfma_bf16_tflops") if bound == "mfma" else pk.get("hbm_read_gbs")
+    return round(achieved / ref, 4) if ref else None
+
+
+def upload_layers(L, S, cfg, layers, dev):
+    """Draws the weights of the given layers on the host cores (a thread pool:
+    the generator releases the GIL for the bulk of the work) and uploads
+    them packed, in order."""
+    import concurrent.futures as cf
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    out = []
+    with cf.ThreadPoolExecutor(n) as ex:
+        for i, lw in enumerate(ex.map(lambda l: S.layer_weights(cfg, l), layers)):
+            out.append(L.weights_from_host(lw, dev))
+            if i % 10 == 9:
+                print(f"# {i + 1} layers uploaded", file=sys.stderr, flush=True)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the layer is a single-GPU kernel path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-
+    if args.peaks:
+        return main_peaks(args)
     if args.workload == "decode40":
-        return main_decode(args)
+        res = run_decode(args, args.layers or 40, args.steps, args.warmup, args.decode_path)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_decode()
+        print(json.dumps(res), flush=True)
+        return
     if args.workload == "stack40":
         return main_stack(args)
+    return main_prefill(args)
 
+
+def main_prefill(args):
     import numpy as np
     import torch
 
@@ -118,12 +182,13 @@ def main():
     cfg = S.CONFIGS[args.workload]
     d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, args.tile_m)
     P = cfg.T * cfg.k
+    n_sets = args.layers or 8
 
     # ---- inputs, resident in HBM before timing
     t_gen = time.time()
-    weights, logits, routers = [], [], []
-    for layer in range(args.layers):
-        weights.append(L.weights_from_host(S.layer_weights(cfg, layer), dev))
+    weights = upload_layers(L, S, cfg, range(n_sets), dev)
+    logits, routers = [], []
+    for layer in range(n_sets):
         if args.router:
             routers.append(torch.from_numpy(S.router_weights(cfg, layer).view(np.int16)).to(dev))
             logits.append(torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev))
@@ -145,7 +210,7 @@ def main():
         ("route", "gate_up", "down", "combine"))
 
     def step(i, ev=None):
-        layer = i % args.layers
+        layer = i % n_sets
         w = weights[layer]
         calls = []
         if args.router:
@@ -208,12 +273,13 @@ def main():
                 and not args.router:
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom}
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                "frac_of_measured": frac_of_measured(bound, achieved)}
 
     # whole-layer fractions: useful flops and the weight bytes one layer must read
     counts = routing.counts.cpu().numpy()
     used = int((counts > 0).sum()) + 1
-    w_bytes = used * 3 * cfg.H * cfg.F * (0.5 + 4.0 / 64)
+    w_bytes = used * expert_bytes(cfg)
     layer_flops = 2.0 * 3 * cfg.H * cfg.F * (P + cfg.T)
     step_s = ms_per_step * 1e-3
 
@@ -235,7 +301,7 @@ def main():
             "workload": args.workload, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E,
             "topk": cfg.k,
             "shared_experts": 1, "group": 64, "tile_m": args.tile_m,
-            "layer_weight_sets": args.layers,
+            "layer_weight_sets": n_sets,
             "logits": "router projection x.Wr^T in the step" if args.router
                       else "given (router_logits)",
             "routing": "logits N(0,1) + per-expert Zipf(1.1) log-bias" if cfg.zipf
@@ -255,10 +321,11 @@ def main():
         "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "roofline": roofline,
     }
+    del weights, logits, routers, ws, routing, out, bf16w
+    torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         import oracle
-        from oracle import build as _ob  # noqa: F401  (oracle is built by __graft_entry__.build)
         lw = S.layer_weights(cfg, 0)
         lg = S.router_logits(cfg, 0)
         xs = S.activations(cfg)
@@ -274,7 +341,212 @@ def main():
             "sample": f"route of all {cfg.T} tokens + forward of {ntok} tokens of layer 0 "
                       f"(dequant of the experts they use included), {c1 - c0:.1f} s",
         }
+
+    if args.workload == WORKLOAD and not (args.no_extra or args.router or args.route_host
+                                          or args.unfused):
+        result["extra"] = {
+            "prefill512": run_prefill_rate(S.CONFIGS["prefill512"], 8, 20, 5),
+            "decode40": run_decode(args, 40, 20, 5, "stack", brief=True),
+        }
     print(json.dumps(result), flush=True)
+
+
+def run_prefill_rate(cfg, n_sets, steps, warmup, tile_m=128):
+    """Route + forward of one layer per step, cycling n_sets weight sets: the
+    layer's tokens/s and the fraction of HBM peak at which it streams the
+    weights of the experts it touches."""
+    import numpy as np
+    import torch
+
+    import int4_grouped_gemm_amd as L
+    from synth import inputs as S
+
+    dev = torch.device("cuda:0")
+    d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, tile_m)
+    weights = upload_layers(L, S, cfg, range(n_sets), dev)
+    logits = [torch.from_numpy(S.router_logits(cfg, layer)).to(dev) for layer in range(n_sets)]
+    x = torch.from_numpy(S.activations(cfg).view(np.int16)).to(dev)
+    routing = L.alloc_routing(d, dev)
+    ws = L.alloc_workspace(d, dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L.lily_moe_route(d, logits[i % n_sets], routing, stream)
+        L.lily_moe_forward(d, weights[i % n_sets], x, routing, out, ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    s = (time.perf_counter() - t0) / steps
+    used = int((routing.counts.cpu().numpy() > 0).sum()) + 1
+    gbs = used * expert_bytes(cfg) / s / 1e9
+    res = {"T": cfg.T, "tokens_per_s": round(cfg.T / s, 1), "us_per_layer": round(s * 1e6, 2),
+           "weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "experts_touched": used, "layer_weight_sets": n_sets, "tile_m": tile_m}
+    del weights, ws, routing
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode(args, n_layers_distinct, steps, warmup, path, brief=False):
+    """Batch-1 decode: one step = the 40 MoE layers of the stack at T = 1.
+    The stack holds n_layers_distinct distinct resident weight sets (40: every
+    layer its own). Each of the 256 steps has its own activations and router
+    logits per layer; all inputs are resident before timing. Exits with an
+    error if a decode barrier gave up (routing.sched[30]): its outputs, and so
+    the timing, would be invalid."""
+    import numpy as np
+    import torch
+
+    import int4_grouped_gemm_amd as L
+    from synth import inputs as S
+
+    L.load()
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS["decode40"]
+    n_layers = cfg.layers
+    d = L.dims(1, cfg.H, cfg.F, cfg.E, cfg.k, 32)
+    t_gen = time.time()
+    weights = upload_layers(L, S, cfg, range(n_layers_distinct), dev)
+    n_steps = warmup + steps
+    logits = torch.from_numpy(np.stack([np.stack([S.router_logits(cfg, layer, step % cfg.steps)
+                                                  for layer in range(n_layers)])
+                                        for step in range(n_steps)])).to(dev)
+    xs = torch.from_numpy(np.stack([S.activations(cfg, step % cfg.steps).view(np.int16)
+                                    for step in range(n_steps)])).to(dev)
+    routing = L.alloc_routing(d, dev)
+    ws = L.alloc_workspace(d, dev)
+    out = torch.empty((1, cfg.H), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    layer_w = [weights[layer % n_layers_distinct] for layer in range(n_layers)]
+    if path == "stack":
+        table = L.layer_table(layer_w, dev)
+        r_st = torch.empty(cfg.H, dtype=torch.float32, device=dev)
+        outs_st = torch.empty((n_layers, cfg.H), dtype=torch.int16, device=dev)
+        ids_st = torch.empty((n_layers, cfg.k), dtype=torch.int32, device=dev)
+        w_st = torch.empty((n_layers, cfg.k), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print(f"# decode inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    def step(i):
+        if path == "stack":
+            L.lily_moe_decode_stack(d, n_layers, table, logits[i], xs[i], r_st, outs_st, ids_st,
+                                    w_st, routing.sched, ws, 1e-6, stream)
+            return
+        for layer in range(n_layers):
+            if path == "fused":
+                L.lily_moe_decode(d, layer_w[layer], logits[i, layer], xs[i], routing, out, ws,
+                                  stream)
+            else:
+                L.lily_moe_route(d, logits[i, layer], routing, stream)
+                L.lily_moe_forward(d, layer_w[layer], xs[i], routing, out, ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if path != "layer" and int(routing.sched[30].item()) != 0:
+        print("decode: a device-wide barrier wait gave up (sched[30] set): the workgroups "
+              "were not all resident, outputs and timing are invalid", file=sys.stderr)
+        sys.exit(3)
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    us_per_layer = ms_per_step * 1e3 / n_layers
+    # weight bytes a layer must read: the k routed experts and the shared one
+    layer_bytes = (cfg.k + 1) * expert_bytes(cfg)
+    gbs = layer_bytes / (us_per_layer * 1e-6) / 1e9
+    del weights, ws, routing, logits, xs, layer_w
+    if path == "stack":
+        del table
+    torch.cuda.empty_cache()
+    paths = {"fused": "lily_moe_decode, one launch per layer",
+             "layer": "lily_moe_route + lily_moe_forward (tile_m 32)",
+             "stack": "lily_moe_decode_stack: 40 layers and the residual glue in one launch"}
+    if brief:
+        return {"us_per_layer": round(us_per_layer, 3), "ms_per_step": round(ms_per_step, 4),
+                "weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "distinct_layers": n_layers_distinct, "path": paths[path]}
+    return {
+        "metric": "MoE-layer decode time per layer (T=1, 40-layer step, int4 g64); % of HBM peak",
+        "value": round(us_per_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode40", "T": 1, "H": cfg.H, "F": cfg.F, "E": cfg.E,
+                   "topk": cfg.k, "layers_per_step": n_layers,
+                   "distinct_layers": n_layers_distinct, "path": paths[path]},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "whole layer", "frac_of_measured": frac_of_measured("hbm", gbs)},
+    }
+
+
+def expert_getter(S, cfg, layer):
+    """Oracle expert getter that draws each requested expert's matrices from
+    its own seeded stream (only the experts a sample routes to)."""
+    cache = {}
+
+    def get(tensor, e):
+        key = (tensor, e)
+        if key not in cache:
+            cache[key] = S.expert_matrix(cfg, layer, e, tensor)
+        return cache[key]
+
+    return get, cache
+
+
+def oracle_chain_sample(cfg, samples, tile_m):
+    """The oracle's layer chain (route, forward, residual glue) for sampled
+    tokens: samples = [(chunk or step, token indices)]. Returns the seconds
+    spent in oracle calls (weight generation excluded) and the count of
+    (token, layer) pairs."""
+    import numpy as np
+
+    import oracle
+    from synth import inputs as S
+
+    x0 = np.concatenate([S.activations(cfg, c)[np.asarray(toks)] for c, toks in samples])
+    r = ((x0.astype(np.uint32) << 16).view(np.float32)).copy()
+    x = oracle.residual_norm(r, None, 1e-6)
+    spent = 0.0
+    for layer in range(cfg.layers):
+        lgs = np.concatenate([S.router_logits(cfg, layer, c)[np.asarray(toks)]
+                              for c, toks in samples])
+        rr = oracle.route(lgs, cfg.k, tile_m)
+        get, cache = expert_getter(S, cfg, layer)
+        for e in set(np.unique(rr["topk_ids"]).tolist()) | {cfg.E}:  # draw outside the timing
+            for t in range(3):
+                get(t, e)
+        c0 = time.perf_counter()
+        rr = oracle.route(lgs, cfg.k, tile_m)
+        _, out = oracle.forward(x, rr["topk_ids"], rr["topk_w"], get, cfg.H, cfg.F, cfg.E)
+        x = oracle.residual_norm(r, out, 1e-6)
+        spent += time.perf_counter() - c0
+        del cache
+    return spent, len(x0) * cfg.layers
+
+
+def cpu_baseline_decode():
+    import oracle
+    from synth import inputs as S
+    cfg = S.CONFIGS["decode40"]
+    steps = list(range(16))
+    spent, n = oracle_chain_sample(cfg, [(s, [0]) for s in steps], 32)
+    return {"value": round(spent * 1e6 / n, 1), "unit": "us/layer", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"sampled: decode steps 0-15 of 256 through all {cfg.layers} layers "
+                      f"(route, forward, residual glue per layer; weight generation excluded), "
+                      f"{spent:.1f} s"}
 
 
 def main_stack(args):
@@ -294,11 +566,7 @@ def main_stack(args):
     cfg = S.CONFIGS["stack40_T8192"]
     d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, args.tile_m)
     t_gen = time.time()
-    weights = []
-    for layer in range(cfg.layers):
-        weights.append(L.weights_from_host(S.layer_weights(cfg, layer), dev))
-        if layer % 10 == 9:
-            print(f"# {layer + 1} layers uploaded", file=sys.stderr, flush=True)
+    weights = upload_layers(L, S, cfg, range(cfg.layers), dev)
     logits = [[torch.from_numpy(S.router_logits(cfg, layer, c)).to(dev) for c in range(cfg.chunks)]
               for layer in range(cfg.layers)]
     x0 = [torch.from_numpy(S.activations(cfg, c).view(np.int16)).to(dev) for c in range(cfg.chunks)]
@@ -335,7 +603,7 @@ def main_stack(args):
     n_tok = cfg.T * cfg.chunks
     layer_flops = 2.0 * 3 * cfg.H * cfg.F * (cfg.k + 1) * n_tok * cfg.layers
     # every chunk-layer touches (nearly) all experts: their weights are read once per chunk
-    w_bytes = (cfg.E + 1) * 3 * cfg.H * cfg.F * (0.5 + 4.0 / 64) * cfg.chunks * cfg.layers
+    w_bytes = (cfg.E + 1) * expert_bytes(cfg) * cfg.chunks * cfg.layers
     result = {
         "metric": "MoE-layer prefill tokens/s per layer (40-layer stack, T=8192 in chunks of "
                   "2048, int4 g64); % of HBM / MFMA peak",
@@ -348,95 +616,88 @@ def main_stack(args):
         "config": {"workload": "stack40", "layers": cfg.layers, "tokens": n_tok,
                    "chunk_tokens": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "topk": cfg.k,
                    "tile_m": args.tile_m, "glue": "r += out; x = bf16(r / rms(r))",
-                   "weights_resident_gb": round(cfg.layers * (cfg.E + 1) * 3 * cfg.H * cfg.F *
-                                                (0.5 + 4.0 / 64) / 1e9, 2)},
+                   "weights_resident_gb": round(cfg.layers * (cfg.E + 1) * expert_bytes(cfg) /
+                                                1e9, 2)},
         "layer": {"mfma_frac": round(layer_flops / s_step / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
                   "hbm_weight_frac": round(w_bytes / s_step / 1e9 / PEAK_HBM_GBS, 4),
                   "prefill_tokens_per_s_whole_stack": round(n_tok / s_step, 1)},
     }
+    del weights, logits, ws, routing
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(40)
+        samples = [(c, sorted(rng.choice(cfg.T, 16, replace=False).tolist()))
+                   for c in range(cfg.chunks)]
+        spent, n = oracle_chain_sample(cfg, samples, args.tile_m)
+        result["cpu_baseline"] = {
+            "value": round(n / spent, 2), "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"sampled: 64 tokens (16 per chunk) through all {cfg.layers} layers "
+                      f"(route, forward, residual glue; weight generation excluded), "
+                      f"{spent:.1f} s; value = token-layers per second"}
     print(json.dumps(result), flush=True)
 
 
-def main_decode(args):
-    """Batch-1 decode: one step = 40 MoE layers at T = 1 (route + forward per
-    layer). The 40 layers cycle through --layers distinct weight sets (8 by
-    default, 3.6 GB), so every layer's weights stream from HBM. Each step and
-    layer has its own router logits; all inputs are resident before timing."""
+def main_peaks(args):
+    """Achievable peaks of this device: MFMA throughput on random operands
+    at 1 and 2 wavefronts per SIMD (with the shader clock from s_memtime
+    against the 100 MHz s_memrealtime), and HBM streaming reads of 4 GiB
+    with plain and LDS-DMA loads (timed with HIP events, median of 5)."""
     import numpy as np
     import torch
 
     import int4_grouped_gemm_amd as L
-    from synth import inputs as S
 
     L.load()
     dev = torch.device("cuda:0")
-    cfg = S.CONFIGS["decode40"]
-    n_layers = cfg.layers
-    d = L.dims(1, cfg.H, cfg.F, cfg.E, cfg.k, 32)
-    weights = [L.weights_from_host(S.layer_weights(cfg, layer), dev) for layer in range(args.layers)]
-    n_steps = args.warmup + args.steps
-    logits = torch.from_numpy(np.stack([np.stack([S.router_logits(cfg, layer, step % cfg.steps)
-                                                  for layer in range(n_layers)])
-                                        for step in range(n_steps)])).to(dev)
-    xs = torch.from_numpy(np.stack([S.activations(cfg, step % cfg.steps).view(np.int16)
-                                    for step in range(n_steps)])).to(dev)
-    routing = L.alloc_routing(d, dev)
-    ws = L.alloc_workspace(d, dev)
-    out = torch.empty((1, cfg.H), dtype=torch.int16, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
-    if args.decode_path == "stack":
-        table = L.layer_table([weights[layer % args.layers] for layer in range(n_layers)], dev)
-        r_st = torch.empty(cfg.H, dtype=torch.float32, device=dev)
-        outs_st = torch.empty((n_layers, cfg.H), dtype=torch.int16, device=dev)
-        ids_st = torch.empty((n_layers, cfg.k), dtype=torch.int32, device=dev)
-        w_st = torch.empty((n_layers, cfg.k), dtype=torch.float32, device=dev)
+    def timed(fn, reps=5):
+        ms = []
+        for _ in range(reps + 1):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ms[1:]))
 
-    def step(i):
-        if args.decode_path == "stack":
-            L.lily_moe_decode_stack(d, n_layers, table, logits[i], xs[i], r_st, outs_st, ids_st,
-                                    w_st, routing.sched, ws, 1e-6, stream)
-            return
-        for layer in range(n_layers):
-            w = weights[layer % args.layers]
-            if args.decode_path == "fused":
-                L.lily_moe_decode(d, w, logits[i, layer], xs[i], routing, out, ws, stream)
-            else:
-                L.lily_moe_route(d, logits[i, layer], routing, stream)
-                L.lily_moe_forward(d, w, xs[i], routing, out, ws, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    us_per_layer = ms_per_step * 1e3 / n_layers
-    # weight bytes a layer must read: the k routed experts and the shared one
-    layer_bytes = (cfg.k + 1) * 3 * cfg.H * cfg.F * (0.5 + 4.0 / 64)
-    gbs = layer_bytes / (us_per_layer * 1e-6) / 1e9
-    result = {
-        "metric": "MoE-layer decode time per layer (T=1, 40-layer step, int4 g64); % of HBM peak",
-        "value": round(us_per_layer, 3),
-        "unit": "us/layer",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "decode40", "T": 1, "H": cfg.H, "F": cfg.F, "E": cfg.E,
-                   "topk": cfg.k, "layers_per_step": n_layers, "layer_weight_sets": args.layers,
-                   "path": {"fused": "lily_moe_decode, one launch per layer",
-                            "layer": "lily_moe_route + lily_moe_forward (tile_m 32)",
-                            "stack": "lily_moe_decode_stack: 40 layers and the residual glue "
-                                     "in one launch"}[args.decode_path]},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "whole layer"},
-    }
-    print(json.dumps(result), flush=True)
+    res = {"device_cus": cus, "mfma": {}, "read": {}}
+    iters = 20000
+    for waves in (4, 8):  # 1 and 2 wavefronts per SIMD
+        sink = torch.empty(cus * waves * 64, dtype=torch.float32, device=dev)
+        times = torch.zeros((cus * waves, 2), dtype=torch.int64, device=dev)
+        ms = timed(lambda: L.lily_calib_mfma(cus, waves, iters, sink, times, stream))
+        t = times.cpu().numpy().astype(np.float64)
+        ghz = float(np.median(t[:, 0] / (t[:, 1] * 10.0)))
+        flops = cus * waves * iters * 8 * 32768.0
+        res["mfma"][f"{waves // 4}_wave_per_simd"] = {
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_ghz": round(ghz, 3),
+            "ms": round(ms, 3)}
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    for grid_mult in (4, 8):
+        grid = cus * grid_mult
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+        for dma in (False, True):
+            ms = timed(lambda: L.lily_calib_read(src, nbytes, grid, dma, sink, stream))
+            res["read"][f"{'lds_dma' if dma else 'plain'}_wg_per_cu_{grid_mult}"] = round(
+                nbytes / (ms * 1e-3) / 1e9, 1)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    res["copy_gbs_read_plus_write"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    res["mfma_bf16_tflops"] = max(v["tflops"] for v in res["mfma"].values())
+    res["hbm_read_gbs"] = max(res["read"].values())
+    res["published"] = {"mfma_bf16_tflops": PEAK_MFMA_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+    if args.write_peaks:
+        with open(PEAKS_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

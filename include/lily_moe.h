@@ -194,7 +194,10 @@ int lily_moe_router(const lily_moe_dims* dims, const uint16_t* w_router, const u
 
 /* Routing of one MoE layer: top-k and softmax per token, histogram,
    exclusive scan, stable scatter and block map, all enqueued on `stream`
-   with no host synchronisation.
+   with no host synchronisation. The router keeps k of E experts per token
+   (Lily articles, section on the three workload shapes: 256 experts, top 8);
+   the histogram, prefix scan, scatter and block map run on the GPU in one
+   command stream without a CPU round trip (section "Prefill").
    logits: fp32 [T, E] router scores. Deterministic and bit-exact for
    finite logits; non-finite logits give unspecified (but in-bounds) output.
    Errors: LILY_ERR_INVALID_ARG (null pointer, bad dims, misalignment),
@@ -218,13 +221,19 @@ int lily_moe_route_host(const lily_moe_dims* dims, const float* logits,
 /* Expert computation of one MoE layer from a routing produced by
    lily_moe_route with the same dims: grouped gate/up GEMM with the int4 ->
    bf16 dequantisation fused into the tile loads, SwiGLU, grouped down GEMM,
-   the shared expert, and the weighted gather-combine.
+   the shared expert, and the weighted gather-combine. The weights are
+   groupwise-affine 4-bit (64 share a bf16 scale and bias) and are rebuilt as
+   bf16 inside the grouped GEMM, on chip, with FP32 accumulation (Lily
+   articles, section "Prefill"); a shared expert processes every token besides
+   the routed ones (section on the three workload shapes).
    x: bf16 bits [T, H]; out: bf16 bits [T, H]; workspace: at least
    lily_moe_workspace_bytes(dims) bytes of device memory (contents on entry
    are ignored). The routing is trusted (ids in range, block map as produced
    by lily_moe_route). Run-to-run deterministic: no floating-point atomics.
    Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (tile_m not 32/64/128,
-   H not a multiple of 256, F not a multiple of 128), LILY_ERR_WORKSPACE,
+   H not a multiple of 256, F not a multiple of 128, or x [T, H], h
+   [T * (topk + 1), F] or one [F, H] matrix as bf16 reaching 4 GiB: the
+   kernels address rows with 32-bit byte offsets), LILY_ERR_WORKSPACE,
    LILY_ERR_HIP. */
 int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
                      const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,

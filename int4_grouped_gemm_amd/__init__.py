@@ -28,7 +28,9 @@ EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_by
            "lily_moe_forward", "lily_moe_dequant", "lily_moe_forward_bf16", "lily_moe_gate_up",
            "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_moe_decode_stack",
            "lily_residual_norm",
-           "lily_last_error")
+           "lily_last_error",
+           # include/lily_calib.h
+           "lily_calib_mfma", "lily_calib_read")
 LILY_SCHED_INTS = 1056 + 64 * 512 + 1
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
@@ -132,6 +134,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                        ctypes.c_void_p]
     lib.lily_last_error.restype = ctypes.c_char_p
     lib.lily_last_error.argtypes = []
+    lib.lily_calib_mfma.restype = ctypes.c_int
+    lib.lily_calib_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_calib_read.restype = ctypes.c_int
+    lib.lily_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -374,6 +382,18 @@ def lily_residual_norm(T: int, H: int, r, out, x_next, eps: float = 1e-6, stream
 
 def lily_last_error() -> str:
     return load().lily_last_error().decode()
+
+
+def lily_calib_mfma(grid: int, waves_per_cu: int, iters: int, sink, times, stream=None) -> None:
+    lib = load()
+    _check(lib.lily_calib_mfma(grid, waves_per_cu, iters, _ptr(sink), _ptr(times),
+                               _stream(stream)), lib)
+
+
+def lily_calib_read(src, nbytes: int, grid: int, dma: bool, sink, stream=None) -> None:
+    lib = load()
+    _check(lib.lily_calib_read(_ptr(src), nbytes, grid, 1 if dma else 0, _ptr(sink),
+                               _stream(stream)), lib)
 
 
 # ----------------------------------------------------------------- allocation

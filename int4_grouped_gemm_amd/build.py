@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblily_moe.so")
 
 SOURCES = ["abi.hip", "route.hip", "route_host.hip", "gemm_w4.hip", "decode.hip", "router.hip",
-           "residual.hip"]
+           "residual.hip", "calib.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",

@@ -145,6 +145,20 @@ static int check_forward_args(const lily_moe_dims* dims, const lily_moe_weights*
         return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 256", dims->H);
     if (dims->F % 128)
         return set_error(LILY_ERR_UNSUPPORTED, "F = %d must be a multiple of 128", dims->F);
+    // The grouped GEMMs address their A rows (x [T, H] for gate/up, h
+    // [T * (topk + 1), F] for down) with 32-bit byte offsets, and the bf16
+    // weight rows of the unfused twin likewise within one [F, H] matrix.
+    const int64_t kMax = (int64_t)1 << 32;
+    const int64_t rows = (int64_t)dims->T * dims->topk + dims->T;
+    if ((int64_t)dims->T * dims->H * 2 >= kMax)
+        return set_error(LILY_ERR_UNSUPPORTED, "x [T = %d, H = %d] bf16 is 4 GiB or more", dims->T,
+                         dims->H);
+    if (rows * dims->F * 2 >= kMax)
+        return set_error(LILY_ERR_UNSUPPORTED,
+                         "h [T * (topk + 1) = %lld, F = %d] bf16 is 4 GiB or more",
+                         (long long)rows, dims->F);
+    if ((int64_t)dims->F * dims->H * 2 >= kMax)
+        return set_error(LILY_ERR_UNSUPPORTED, "an [F, H] bf16 matrix is 4 GiB or more");
     return LILY_OK;
 }
 

@@ -10,7 +10,7 @@ import pytest
 import int4_grouped_gemm_amd as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lily_moe.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("lily_moe.h", "lily_calib.h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,9 +22,16 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lily_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(lily_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_header_is_checked():
+    assert sorted(os.path.basename(h) for h in HEADERS) == \
+        sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -178,6 +185,41 @@ def test_forward_rejects(lib):
     assert str(need) in lib.lily_last_error().decode()
     assert lib.lily_moe_forward(ctypes.byref(d), None, FAKE, ctypes.byref(routing()), FAKE, FAKE,
                                 need, None) == L.LILY_ERR_INVALID_ARG
+
+
+def test_forward_rejects_32bit_offsets(lib):
+    """Shapes whose A rows the GEMMs cannot reach with 32-bit byte offsets are
+    rejected on the host before any launch (x [T, H] or h [T (k + 1), F] of
+    4 GiB or more)."""
+    big_x = good_dims(T=1 << 20, H=2048, F=512, E=256, topk=8, tile_m=128)
+    assert call_forward(lib, big_x) == L.LILY_ERR_UNSUPPORTED
+    assert "x [T = 1048576" in lib.lily_last_error().decode()
+    just_x = good_dims(T=(1 << 20) - 1, H=2048, F=128, E=256, topk=1, tile_m=128)
+    rc = call_forward(lib, just_x, nbytes=0)  # passes the shape checks, fails on the workspace
+    assert rc == L.LILY_ERR_WORKSPACE, lib.lily_last_error().decode()
+    big_h = good_dims(T=466_034, H=256, F=512, E=256, topk=8, tile_m=128)  # 9 T * 1024 >= 2^32
+    assert call_forward(lib, big_h) == L.LILY_ERR_UNSUPPORTED
+    assert "h [T * (topk + 1) = 4194306" in lib.lily_last_error().decode()
+    ok_h = good_dims(T=466_033, H=256, F=512, E=256, topk=8, tile_m=128)
+    rc = call_forward(lib, ok_h, nbytes=0)  # passes the shape checks, fails on the workspace
+    assert rc == L.LILY_ERR_WORKSPACE, lib.lily_last_error().decode()
+    for fn in (lib.lily_moe_gate_up,):
+        assert fn(ctypes.byref(big_x), ctypes.byref(weights()), FAKE, ctypes.byref(routing()), FAKE,
+                  1 << 40, None) == L.LILY_ERR_UNSUPPORTED
+    assert lib.lily_moe_down(ctypes.byref(big_h), ctypes.byref(weights()), ctypes.byref(routing()),
+                             FAKE, 1 << 40, None) == L.LILY_ERR_UNSUPPORTED
+    assert lib.lily_moe_forward_bf16(ctypes.byref(big_x), ctypes.byref(weights()), FAKE,
+                                     ctypes.byref(routing()), FAKE, FAKE, 1 << 40,
+                                     None) == L.LILY_ERR_UNSUPPORTED
+
+
+def test_calib_rejects(lib):
+    assert lib.lily_calib_mfma(0, 4, 100, FAKE, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_mfma(256, 4, 101, FAKE, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_mfma(256, 4, 100, None, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_read(FAKE, 1000, 256, 0, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_read(FAKE + 4, 1024, 256, 1, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_read(None, 1024, 256, 1, FAKE, None) == L.LILY_ERR_INVALID_ARG
 
 
 def test_residual_norm_rejects(lib):

@@ -126,7 +126,8 @@ def test_decode_stack_one_launch(step):
     against the oracle's chain of the same layers: routing exact, every
     layer's output within the tolerance; against the per-layer launches
     (lily_moe_decode + lily_residual_norm): routing identical and outputs
-    compared; run twice bit-identically; barrier counters left zero."""
+    identical bit for bit, final residual included; run twice
+    bit-identically; barrier counters left zero."""
     cfg = S.CONFIGS["decode40"]
     n_layers = 16
     dev = torch.device("cuda")
@@ -173,6 +174,10 @@ def test_decode_stack_one_launch(step):
         chain.append(out.cpu().numpy()[0].copy())
     same = sum(np.array_equal(c, o) for c, o in zip(chain, outs_s))
     _flush(f"  layers bit-identical to the per-layer launches: {same} of {n_layers}")
+    assert same == n_layers, "the one-launch stack must equal the per-layer launches bit for bit"
+    assert np.array_equal(r.cpu().numpy().reshape(-1).view(np.uint32),
+                          r_s.reshape(-1).view(np.uint32)), \
+        "final residual differs from the per-layer chain's"
 
     # the oracle's chain
     ora_r = G.bf16_bits_to_f64(x0).astype(np.float32).reshape(1, cfg.H)
