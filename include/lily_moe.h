@@ -309,6 +309,28 @@ int lily_moe_decode(const lily_moe_dims* dims, const lily_moe_weights* weights,
                     const float* logits, const uint16_t* x, const lily_moe_routing* routing,
                     uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* lily_moe_decode for callers that cannot allocate device memory (code
+   under HIP graph capture, serving loops and harnesses that forbid hipMalloc):
+   the same routing and output (the same kernel), but the scratch that
+   lily_moe_decode takes from its workspace and routing.sched (the h rows and
+   the device-wide barrier's counters) lives in a static device array of the
+   library, LILY_DECODE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU holds
+   from its first call until the process ends. The call allocates nothing and
+   clears the counters itself (a small kernel, no memset). Every call on a GPU
+   shares that GPU's array: calls that overlap on one GPU (several streams or
+   threads) race and give wrong results; order them on one stream.
+   logits fp32 [T, E], x bf16 [T, H]; topk_ids int32 [T, topk] and topk_w fp32
+   [T, topk] receive the routing; out bf16 [T, H]; status: NULL or one int32
+   of device memory, set to 0 and then to 1 if the barrier wait gave up after
+   half a second (the outputs are then invalid). Sizes as lily_moe_decode;
+   T * (topk + 1) * F bf16 must fit the scratch's 131072-byte h area (which
+   the size rules of lily_moe_decode already ensure). Errors:
+   LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED, LILY_ERR_HIP. */
+#define LILY_DECODE_NOALLOC_SCRATCH_BYTES (4096 + 131072)
+int lily_moe_decode_noalloc(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                            const float* logits, const uint16_t* x, int32_t* topk_ids,
+                            float* topk_w, uint16_t* out, int32_t* status, void* stream);
+
 /* Batch-1 decode through a stack of MoE layers in one launch (T = 1): for
    l = 0 .. n_layers - 1, x_l = bf16(r_l / sqrt(mean(r_l^2) + eps)) with
    r_0 = x0, out_l = the MoE layer l of lily_moe_decode on x_l, and

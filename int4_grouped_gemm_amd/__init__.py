@@ -26,7 +26,8 @@ LILY_ERR_HIP = -4
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
            "lily_w4_pack", "lily_moe_router", "lily_moe_route", "lily_moe_route_host",
            "lily_moe_forward", "lily_moe_dequant", "lily_moe_forward_bf16", "lily_moe_gate_up",
-           "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_moe_decode_stack",
+           "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_moe_decode_noalloc",
+           "lily_moe_decode_stack",
            "lily_residual_norm",
            "lily_last_error",
            # include/lily_calib.h
@@ -134,6 +135,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                        ctypes.c_void_p]
     lib.lily_last_error.restype = ctypes.c_char_p
     lib.lily_last_error.argtypes = []
+    lib.lily_moe_decode_noalloc.restype = ctypes.c_int
+    lib.lily_moe_decode_noalloc.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.lily_calib_mfma.restype = ctypes.c_int
     lib.lily_calib_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
@@ -354,6 +359,15 @@ def lily_moe_decode(d: LilyMoeDims, weights: Weights, logits, x, routing: Routin
     rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(logits), _ptr(x),
                              ctypes.byref(routing.c()), _ptr(out), _ptr(workspace),
                              _ws_bytes(workspace), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_decode_noalloc(d: LilyMoeDims, weights: Weights, logits, x, topk_ids, topk_w, out,
+                            status=None, stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_decode_noalloc(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(logits),
+                                     _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(out),
+                                     _ptr(status), _stream(stream))
     _check(rc, lib)
 
 

@@ -46,6 +46,9 @@ ForwardWorkspace forward_workspace_split(const lily_moe_dims& d, void* ws);
 size_t packed_w4_bytes(int n, int N, int K);
 int launch_pack(const lily_w4& w, int n, int N, int K, void* packed, hipStream_t stream);
 int decode_supported(const lily_moe_dims& d);
+int launch_decode_noalloc(const lily_moe_dims& d, const lily_moe_weights& w, const float* logits,
+                          const uint16_t* x, int32_t* topk_ids, float* topk_w, uint16_t* out,
+                          int32_t* status, hipStream_t stream);
 int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float* logits,
                   const uint16_t* x, const lily_moe_routing& r, uint16_t* out, void* workspace,
                   hipStream_t stream);
@@ -357,6 +360,30 @@ int lily_moe_decode(const lily_moe_dims* dims, const lily_moe_weights* weights,
     if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
     return launch_decode(*dims, *weights, logits, x, *routing, out, workspace,
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_moe_decode_noalloc(const lily_moe_dims* dims, const lily_moe_weights* weights,
+                            const float* logits, const uint16_t* x, int32_t* topk_ids,
+                            float* topk_w, uint16_t* out, int32_t* status, void* stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if ((rc = decode_supported(*dims))) return rc;
+    if (!weights) return set_error(LILY_ERR_INVALID_ARG, "weights is NULL");
+    if ((rc = check_packed(weights->gate, "gate")) || (rc = check_packed(weights->up, "up")) ||
+        (rc = check_packed(weights->down, "down")) ||
+        (rc = check_packed(weights->sh_gate, "sh_gate")) ||
+        (rc = check_packed(weights->sh_up, "sh_up")) ||
+        (rc = check_packed(weights->sh_down, "sh_down")))
+        return rc;
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(out);
+    if (status && ((uintptr_t)status & 3))
+        return set_error(LILY_ERR_INVALID_ARG, "status is not 4-byte aligned");
+    return launch_decode_noalloc(*dims, *weights, logits, x, topk_ids, topk_w, out, status,
+                                 reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_residual_norm(int32_t T, int32_t H, float* r, const uint16_t* out, uint16_t* x_next,

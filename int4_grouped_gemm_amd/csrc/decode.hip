@@ -23,6 +23,8 @@
 // counted in at the barrier, so that they arrive while it waits.
 // Row r of the layer is token r / (k + 1), slot r % (k + 1): slots 0..k-1
 // are the routed experts in top-k order, slot k the shared expert.
+#include <mutex>
+
 #include "common.hpp"
 #include "topk.hpp"
 #include "w4.hpp"
@@ -859,9 +861,13 @@ int decode_supported(const lily_moe_dims& d) {
     return LILY_OK;
 }
 
-int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float* logits,
-                  const uint16_t* x, const lily_moe_routing& r, uint16_t* out, void* workspace,
-                  hipStream_t stream) {
+// The launch of lily_moe_decode and lily_moe_decode_noalloc: h [T (k + 1),
+// F] bf16 scratch, bar / grp / err the device-wide barrier's counters (zero
+// on entry, left zero) and its give-up flag.
+static int launch_decode_with(const lily_moe_dims& d, const lily_moe_weights& w,
+                              const float* logits, const uint16_t* x, int32_t* topk_ids,
+                              float* topk_w, uint16_t* out, uint16_t* h, int32_t* bar,
+                              int32_t* grp, int32_t* err, hipStream_t stream) {
     DecodeArgs a{};
     a.logits = logits;
     a.x = x;
@@ -876,14 +882,13 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
     a.sh_gate = static_cast<const char*>(w.sh_gate);
     a.sh_up = static_cast<const char*>(w.sh_up);
     a.sh_down = static_cast<const char*>(w.sh_down);
-    a.topk_ids = r.topk_ids;
-    a.topk_w = r.topk_w;
-    a.h = static_cast<uint16_t*>(workspace);
+    a.topk_ids = topk_ids;
+    a.topk_w = topk_w;
+    a.h = h;
     a.out = out;
-    a.bar = r.sched + kDecodeBarrier;
-    a.grp = r.sched + kQueueInts;
-    a.err = r.sched + kDecodeBarrier + 2;
-    static_assert(kQueueInts + kBarGroups * kBarLine <= kSchedInts, "barrier group counters");
+    a.bar = bar;
+    a.grp = grp;
+    a.err = err;
     const int g = decode_grid();
     // (checked here, after the arguments: it depends on the device)
     const long units = (long)d.T * (d.topk + 1) * (d.F / 8);
@@ -896,6 +901,77 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
     // device-wide barrier relies on.
     hipLaunchKernelGGL(moe_decode_kernel, dim3((unsigned)g), dim3(kDecThreads), 0, stream, a);
     return check_launch("decode");
+}
+
+int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float* logits,
+                  const uint16_t* x, const lily_moe_routing& r, uint16_t* out, void* workspace,
+                  hipStream_t stream) {
+    static_assert(kQueueInts + kBarGroups * kBarLine <= kSchedInts, "barrier group counters");
+    return launch_decode_with(d, w, logits, x, r.topk_ids, r.topk_w, out,
+                              static_cast<uint16_t*>(workspace), r.sched + kDecodeBarrier,
+                              r.sched + kQueueInts, r.sched + kDecodeBarrier + 2, stream);
+}
+
+// Scratch of lily_moe_decode_noalloc, for callers that cannot allocate: the
+// barrier counters (kNoAllocCtrInts ints, laid out as in a routing's sched
+// array), then h of up to kDecodeMaxT tokens. Each GPU the library runs on
+// holds its own copy until the process ends. Host code never uses the
+// array's name as an address: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, once per device.
+constexpr int kNoAllocCtrInts = 1024;
+constexpr size_t kNoAllocHBytes = (size_t)kDecodeMaxT * 2 * kDecLdsWords * sizeof(uint16_t);
+constexpr size_t kNoAllocBytes = kNoAllocCtrInts * sizeof(int32_t) + kNoAllocHBytes;
+static_assert(kQueueInts + kBarGroups * kBarLine <= kNoAllocCtrInts &&
+                  kDecodeBarrier + 3 <= kNoAllocCtrInts, "no-alloc barrier counters");
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static char* g_scratch[kNoAllocMaxDevices];
+
+static int scratch_of_device(char** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices)
+        return set_error(LILY_ERR_HIP, "decode_noalloc: no current device below %d",
+                         kNoAllocMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return set_error(LILY_ERR_HIP, "decode_noalloc: hipGetSymbolAddress: %s",
+                             hipGetErrorString(e));
+        g_scratch[dev] = static_cast<char*>(p);
+    }
+    *out = g_scratch[dev];
+    return LILY_OK;
+}
+
+// Clears the barrier counters (a kernel rather than a memset, so that the
+// call also behaves under graph capture) and the caller's status word.
+__global__ void __launch_bounds__(256) clear_ints_kernel(int32_t* p, int n, int32_t* status) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+    if (status && threadIdx.x == 0) *status = 0;
+}
+
+int launch_decode_noalloc(const lily_moe_dims& d, const lily_moe_weights& w, const float* logits,
+                          const uint16_t* x, int32_t* topk_ids, float* topk_w, uint16_t* out,
+                          int32_t* status, hipStream_t stream) {
+    const size_t need = (size_t)d.T * (d.topk + 1) * d.F * sizeof(uint16_t);
+    if (need > kNoAllocHBytes)
+        return set_error(LILY_ERR_UNSUPPORTED,
+                         "decode_noalloc: h of T * (topk + 1) * F = %zu bytes exceeds the %zu-byte "
+                         "scratch", need, kNoAllocHBytes);
+    char* base = nullptr;
+    int rc = scratch_of_device(&base);
+    if (rc) return rc;
+    int32_t* ctr = reinterpret_cast<int32_t*>(base);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base + kNoAllocCtrInts * sizeof(int32_t));
+    hipLaunchKernelGGL(clear_ints_kernel, dim3(1), dim3(256), 0, stream, ctr, kNoAllocCtrInts,
+                       status);
+    if ((rc = check_launch("decode_noalloc clear"))) return rc;
+    return launch_decode_with(d, w, logits, x, topk_ids, topk_w, out, h, ctr + kDecodeBarrier,
+                              ctr + kQueueInts, status ? status : ctr + kDecodeBarrier + 2, stream);
 }
 
 int decode_stack_supported(const lily_moe_dims& d, int n_layers) {
