@@ -236,9 +236,48 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
             wait_lgkmcnt0();
             return;
         }
-        // The weights' LDS reads are issued first and each sub-step's A
-        // fragments one sub-step ahead; the MFMAs of sub-step s run while
-        // the weights of sub-step s + 1 are dequantised.
+        if constexpr (MIA <= 2) {
+            // Few rows: the step is bound by the dequantisation, so all
+            // 4 x NI words of the step are rebuilt first, as independent
+            // chains that the VALU can issue back to back, then the MFMAs
+            // run on A fragments read meanwhile.
+            u32x4 q[NI];
+            float s512[NI], bias[NI];
+#pragma unroll
+            for (int g = 0; g < NI; ++g) {
+                q[g] = *reinterpret_cast<const u32x4*>(Qb + q_rd[g]);
+                s512[g] = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + sb_rd[g])) * 512.0f;
+                bias[g] = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + 512 + sb_rd[g]));
+            }
+            bf16x8 af[4][MIA];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int i = 0; i < MIA; ++i)
+                    af[s4][i] = *reinterpret_cast<const bf16x8*>(Ab + i * 4096 + a_rd[s4]);
+            bf16x8 bfr[4][NI];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int g = 0; g < NI; ++g) {
+                    uint32_t w[4];
+                    dequant8(q[g][s4], s512[g], bias[g], w);
+                    bfr[s4][g] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+                }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int i = 0; i < MIA; ++i)
+#pragma unroll
+                    for (int g = 0; g < NI; ++g)
+                        acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s4][g], af[s4][i],
+                                                                            acc[i][g], 0, 0, 0);
+            wait_lgkmcnt0();
+            return;
+        }
+        // Full tiles: the weights' LDS reads are issued first and each
+        // sub-step's A fragments one sub-step ahead; the MFMAs of sub-step s
+        // run while the weights of sub-step s + 1 are dequantised.
         u32x4 q[NI];
         uint16_t sbits[NI], bbits[NI];
 #pragma unroll
