@@ -335,21 +335,25 @@ int lily_moe_decode_noalloc(const lily_moe_dims* dims, const lily_moe_weights* w
    l = 0 .. n_layers - 1, x_l = bf16(r_l / sqrt(mean(r_l^2) + eps)) with
    r_0 = x0, out_l = the MoE layer l of lily_moe_decode on x_l, and
    r_{l+1} = r_l + out_l (fp32): the chain of lily_moe_decode and
-   lily_residual_norm launches, in one launch whose workgroups (one per
-   compute unit, all resident, as for lily_moe_decode) pass two device-wide
-   barriers per layer. The next layer's top-k and gate/up weight loads are
-   issued while the current layer's down phase runs (the pages run a decode
-   step as one concurrent pass: Lily articles, section "Decode").
+   lily_residual_norm launches (bit for bit), in one launch whose workgroups
+   (one per compute unit, all resident) exchange h and out through the
+   workspace twice per layer, while each layer's weights stream into LDS a
+   layer or more ahead (the pages run a decode step as one concurrent pass:
+   Lily articles, section "Decode").
    layers: device array of n_layers lily_moe_weights (packed stacks, as for
    lily_moe_decode); logits fp32 [n_layers][E]; x0 bf16 [H]; r fp32 [H]
    (ignored on entry, r_{n_layers} on exit); outs bf16 [n_layers][H] (each
    layer's output); topk_ids int32 and topk_w fp32 [n_layers][topk] (each
    layer's routing); sched: as in lily_moe_routing (its barrier counters are
-   zero on entry and left zero; sched[30] is set to 1 if a barrier wait gave
-   up after half a second, which makes the outputs invalid).
-   Needs T = 1, H a multiple of 512 (at most 2048), F a multiple of 256 with
-   (topk + 1) * F <= 16384, and (topk + 1) * F / 8 at most four per compute
-   unit. workspace: lily_moe_workspace_bytes(dims) bytes.
+   zero on entry and left zero; sched[30] is set to 1 if a wait, for the
+   start barrier or an exchange, gave up after half a second, which makes the
+   outputs invalid). workspace: lily_moe_workspace_bytes(dims) bytes; its
+   exchange area is cleared by the launch itself.
+   Needs T = 1, n_layers * topk <= 1024, H a multiple of 512 (at most 2048
+   and at most 8 per compute unit), F a multiple of 256 with
+   (topk + 1) * F <= 4608, and the gate/up units ((topk + 1) * F / 8 sets of
+   8 features, dealt over the compute units) at most 4 per compute unit and
+   within a 54 KB LDS buffer (3 at H = 2048).
    Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED, LILY_ERR_WORKSPACE,
    LILY_ERR_HIP. */
 int lily_moe_decode_stack(const lily_moe_dims* dims, int32_t n_layers,
