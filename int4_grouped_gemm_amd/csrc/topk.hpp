@@ -41,32 +41,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(max(a, b), max(c, d));
 }
 
-// Top-k and softmax of one token by one wavefront, NPER = ceil(E / 64)
-// logits per lane. Lane l holds the logits of experts l, l + 64, ... as
+// The k largest of one token's logits and their softmax, by one wavefront,
+// from lv: lane l holds the logits of experts l, l + 64, ... (NPER =
+// ceil(E / 64) per lane; entries past E are ignored). They become
 // order-preserving keys; a taken expert's key becomes 0, below every real
 // key. Each round takes the wavefront maximum and, among the experts holding
-// it, the lowest index (ballots in expert order).
-// hist, when not null, counts the chosen experts (integer atomics: the
-// totals do not depend on their order).
+// it, the lowest index (ballots in expert order). Lane j < k receives slot
+// j: my_id and my_w.
 template <int NPER>
-__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
-                                           int32_t* __restrict__ topk_ids,
-                                           float* __restrict__ topk_w, int32_t* hist) {
+__device__ __forceinline__ void topk_select(const float (&lv)[NPER], int E, int k, int& my_id,
+                                            float& my_w) {
     const int lane = threadIdx.x % kWave;
-    const float* row = logits + (size_t)t * E;
-    // Every lane issues all its loads before the first use (indexes clamped
-    // into the row, so none is conditional); a load per branch would wait
-    // for each one in turn.
-    float lv[NPER];
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-        const int e = lane + i * kWave;
-        lv[i] = row[e < E ? e : E - 1];
-    }
     uint32_t key[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) key[i] = (lane + i * kWave < E) ? ordered_bits(lv[i]) : 0u;
-    int my_id = 0;
+    my_id = 0;
     float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
         uint32_t best = key[0];
@@ -97,9 +86,41 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
     const float ex = expf(my_l - l0);
     float sum = 0.0f;
     for (int j = 0; j < k; ++j) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+    my_w = ex / sum;
+}
+
+// Loads token t's logits for topk_select. Every lane issues all its loads
+// before the first use (indexes clamped into the row, so none is
+// conditional); a load per branch would wait for each one in turn.
+template <int NPER>
+__device__ __forceinline__ void topk_load(const float* __restrict__ logits, int t, int E,
+                                          float (&lv)[NPER]) {
+    const int lane = threadIdx.x % kWave;
+    const float* row = logits + (size_t)t * E;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int e = lane + i * kWave;
+        lv[i] = row[e < E ? e : E - 1];
+    }
+}
+
+// Top-k and softmax of one token by one wavefront (topk_load, topk_select),
+// written to topk_ids / topk_w [t * k + slot]. hist, when not null, counts
+// the chosen experts (integer atomics: the totals do not depend on their
+// order).
+template <int NPER>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
+                                           int32_t* __restrict__ topk_ids,
+                                           float* __restrict__ topk_w, int32_t* hist) {
+    const int lane = threadIdx.x % kWave;
+    float lv[NPER];
+    topk_load<NPER>(logits, t, E, lv);
+    int my_id;
+    float my_w;
+    topk_select<NPER>(lv, E, k, my_id, my_w);
     if (lane < k) {
         topk_ids[(size_t)t * k + lane] = my_id;
-        topk_w[(size_t)t * k + lane] = ex / sum;
+        topk_w[(size_t)t * k + lane] = my_w;
         if (hist) atomicAdd(hist + my_id, 1);
     }
 }
