@@ -1,8 +1,9 @@
 """Benchmark of the int4 grouped-GEMM MoE layer on one MI355X.
 
 One step = one pass of the whole hot path over one batch: lily_moe_route
-(top-k, softmax, histogram, scan, scatter, block map) then the three stages
-of lily_moe_forward (gate/up + SwiGLU, down, combine) for one MoE layer of
+(top-k, softmax, histogram, scan, scatter, block map) then the stages of
+lily_moe_forward (lily_moe_ffn: gate/up + SwiGLU and down in one launch;
+lily_moe_combine) for one MoE layer of
 T = 2048 tokens (H 2048, F 512, 256 experts top-8 + 1 shared, int4 g64,
 router logits N(0,1) plus a Zipf(1.1) log-bias per expert). Steps cycle
 through several distinct layer weight sets (8 by default, 3.6 GB) so that
@@ -77,6 +78,9 @@ def parse():
     ap.add_argument("--route-host", action="store_true",
                     help="ablation: route with lily_moe_route_host (histogram, scan, scatter and "
                          "block map on the host after a stream synchronisation)")
+    ap.add_argument("--separate-gemms", action="store_true",
+                    help="time gate/up and down as two launches (lily_moe_gate_up, "
+                         "lily_moe_down) instead of lily_moe_ffn")
     ap.add_argument("--unfused", action="store_true",
                     help="ablation: lily_moe_dequant (bf16 weights of the used experts to HBM) "
                          "then lily_moe_forward_bf16 (the same GEMMs on bf16 tiles); tile_m 32 "
@@ -105,6 +109,7 @@ def stage_work(cfg, P):
         "route": ("hbm", cfg.T * cfg.E * 4 + P * 4 * 4 + cfg.T * cfg.k * 4),
         "gate_up": ("mfma", 2.0 * rows * cfg.H * 2 * cfg.F),
         "down": ("mfma", 2.0 * rows * cfg.F * cfg.H),
+        "ffn": ("mfma", 2.0 * rows * cfg.H * 3 * cfg.F),
         "combine": ("hbm", rows * cfg.H * 4 + cfg.T * cfg.H * 2 + P * 8),
         # unfused twin: the packed weights of every expert read (upper bound:
         # only used ones are) and their bf16 written; then both GEMMs
@@ -207,7 +212,8 @@ def main_prefill(args):
     stream = torch.cuda.current_stream()
     stages = (("router",) if args.router else ()) + (
         ("route", "dequant", "forward_bf16") if args.unfused else
-        ("route", "gate_up", "down", "combine"))
+        ("route", "gate_up", "down", "combine") if args.separate_gemms else
+        ("route", "ffn", "combine"))
 
     def step(i, ev=None):
         layer = i % n_sets
@@ -221,9 +227,12 @@ def main_prefill(args):
             calls += [lambda: L.lily_moe_dequant(d, w, routing, bf16w, stream),
                       lambda: L.lily_moe_forward_bf16(d, bf16w, x, routing, out, ws,
                                                       stream=stream)]
-        else:
+        elif args.separate_gemms:
             calls += [lambda: L.lily_moe_gate_up(d, w, x, routing, ws, stream),
                       lambda: L.lily_moe_down(d, w, routing, ws, stream),
+                      lambda: L.lily_moe_combine(d, routing, ws, out, stream)]
+        else:
+            calls += [lambda: L.lily_moe_ffn(d, w, x, routing, ws, stream),
                       lambda: L.lily_moe_combine(d, routing, ws, out, stream)]
         for j, call in enumerate(calls):
             if ev is not None:

@@ -239,15 +239,24 @@ int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
                      const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* The three stages of lily_moe_forward, callable one at a time (for example
-   to time each stage). lily_moe_forward runs exactly these kernels in this
-   order on the same workspace (layout under lily_moe_workspace_bytes).
+/* The stages of lily_moe_forward, callable one at a time (for example to
+   time each stage), on the same workspace (layout under
+   lily_moe_workspace_bytes). lily_moe_forward runs lily_moe_ffn, then
+   lily_moe_combine.
    P = T * topk; rows 0..P-1 are the routed (token, expert) pairs in expert
    order (row r = pair sorted_pairs[r]); rows P..P+T-1 are the shared
    expert's rows for tokens 0..T-1.
    lily_moe_gate_up: h[r] = bf16(silu(x Wg^T) * (x Wu^T)) with the weights
      dequantised tile by tile on chip;
    lily_moe_down: y[r] = h[r] Wd^T in fp32;
+   lily_moe_ffn: both of them, h then y, bit for bit as the two calls in
+     turn. When neither GEMM splits K (large T; the split depends on the
+     sizes only) and the schedule has at most 1024 blocks, it is one launch
+     in which a workgroup moves from gate/up tiles to down tiles as the
+     gate/up work runs out; a down tile waits for its block's gate/up tiles
+     (a bounded wait that can only give up on a faulty device: then it sets
+     routing->sched[30] and the output is not valid). Otherwise it is the
+     two launches;
    lily_moe_combine: out[t] = bf16(y[P + t] + sum_j topk_w[t, j] *
      y[pair_rows[t * topk + j]]), fp32 sum in slot order; out: bf16 [T, H].
    Errors as for lily_moe_forward. */
@@ -257,6 +266,9 @@ int lily_moe_gate_up(const lily_moe_dims* dims, const lily_moe_weights* weights,
 int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
                   const lily_moe_routing* routing, void* workspace, size_t workspace_bytes,
                   void* stream);
+int lily_moe_ffn(const lily_moe_dims* dims, const lily_moe_weights* weights, const uint16_t* x,
+                 const lily_moe_routing* routing, void* workspace, size_t workspace_bytes,
+                 void* stream);
 int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,
                      void* workspace, size_t workspace_bytes, uint16_t* out, void* stream);
 

@@ -26,7 +26,7 @@ LILY_ERR_HIP = -4
 EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_bytes",
            "lily_w4_pack", "lily_moe_router", "lily_moe_route", "lily_moe_route_host",
            "lily_moe_forward", "lily_moe_dequant", "lily_moe_forward_bf16", "lily_moe_gate_up",
-           "lily_moe_down", "lily_moe_combine", "lily_moe_decode", "lily_moe_decode_noalloc",
+           "lily_moe_down", "lily_moe_ffn", "lily_moe_combine", "lily_moe_decode", "lily_moe_decode_noalloc",
            "lily_moe_decode_stack",
            "lily_residual_norm",
            "lily_last_error",
@@ -116,6 +116,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_moe_down.restype = ctypes.c_int
     lib.lily_moe_down.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), P(LilyMoeRouting),
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.lily_moe_ffn.restype = ctypes.c_int
+    lib.lily_moe_ffn.argtypes = [P(LilyMoeDims), P(LilyMoeWeights), ctypes.c_void_p,
+                                 P(LilyMoeRouting), ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]
     lib.lily_moe_combine.restype = ctypes.c_int
     lib.lily_moe_combine.argtypes = [P(LilyMoeDims), P(LilyMoeRouting), ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
@@ -342,6 +346,15 @@ def lily_moe_down(d: LilyMoeDims, weights: Weights, routing: Routing, workspace,
     lib = load()
     rc = lib.lily_moe_down(ctypes.byref(d), ctypes.byref(weights.c()), ctypes.byref(routing.c()),
                            _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+    _check(rc, lib)
+
+
+def lily_moe_ffn(d: LilyMoeDims, weights: Weights, x, routing: Routing, workspace,
+                 stream=None) -> None:
+    lib = load()
+    rc = lib.lily_moe_ffn(ctypes.byref(d), ctypes.byref(weights.c()), _ptr(x),
+                          ctypes.byref(routing.c()), _ptr(workspace), _ws_bytes(workspace),
+                          _stream(stream))
     _check(rc, lib)
 
 

@@ -32,6 +32,9 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
                    hipStream_t stream, bool w4);
 int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_moe_routing& r,
                 int max_blocks, const ForwardWorkspace& ws, hipStream_t stream, bool w4);
+int launch_ffn(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+               const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
+               hipStream_t stream);
 int launch_dequant(const void* packed, int n, int N, int K, const int32_t* counts, void* out,
                    hipStream_t stream);
 int decode_stack_supported(const lily_moe_dims& d, int n_layers);
@@ -242,6 +245,16 @@ int lily_moe_route_host(const lily_moe_dims* dims, const float* logits,
     return launch_route_host(*dims, logits, *routing, reinterpret_cast<hipStream_t>(stream));
 }
 
+// G1-G3: one launch where it applies, else gate/up then down.
+static int run_ffn(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+                   const lily_moe_routing& r, const ForwardWorkspace& ws, hipStream_t s) {
+    const int mb = max_blocks_of(d);
+    const int rc = launch_ffn(d, w, x, r, mb, ws, s);
+    if (rc <= 0) return rc;  // launched (0) or failed; 1: not applicable
+    const int rg = launch_gate_up(d, w, x, r, mb, ws, s, true);
+    return rg ? rg : launch_down(d, w, r, mb, ws, s, true);
+}
+
 int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
                      const uint16_t* x, const lily_moe_routing* routing, uint16_t* out,
                      void* workspace, size_t workspace_bytes, void* stream) {
@@ -252,9 +265,7 @@ int lily_moe_forward(const lily_moe_dims* dims, const lily_moe_weights* weights,
     if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
     const ForwardWorkspace ws = forward_workspace_split(*dims, workspace);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int mb = max_blocks_of(*dims);
-    if ((rc = launch_gate_up(*dims, *weights, x, *routing, mb, ws, s, true))) return rc;
-    if ((rc = launch_down(*dims, *weights, *routing, mb, ws, s, true))) return rc;
+    if ((rc = run_ffn(*dims, *weights, x, *routing, ws, s))) return rc;
     return launch_combine(*dims, ws, *routing, out, s);
 }
 
@@ -322,6 +333,17 @@ int lily_moe_down(const lily_moe_dims* dims, const lily_moe_weights* weights,
     return launch_down(*dims, *weights, *routing, max_blocks_of(*dims),
                        forward_workspace_split(*dims, workspace),
                        reinterpret_cast<hipStream_t>(stream), true);
+}
+
+int lily_moe_ffn(const lily_moe_dims* dims, const lily_moe_weights* weights, const uint16_t* x,
+                 const lily_moe_routing* routing, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    int rc = check_forward_args(dims, weights, routing);
+    if (rc) return rc;
+    REQUIRE_PTR(x);
+    if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
+    return run_ffn(*dims, *weights, x, *routing, forward_workspace_split(*dims, workspace),
+                   reinterpret_cast<hipStream_t>(stream));
 }
 
 int lily_moe_combine(const lily_moe_dims* dims, const lily_moe_routing* routing,

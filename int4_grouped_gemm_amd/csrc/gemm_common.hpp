@@ -29,6 +29,12 @@ struct GemmArgs {
     int kc;
     float* part;
     int32_t* tile_ctr;
+    // Gate/up and down in one launch: per schedule block, the gate/up tiles
+    // that have stored their h rows; a down item of the block starts once
+    // all of them have (blk_need tiles). NULL in the separate launches.
+    int32_t* blk_done;
+    int blk_need;
+    int32_t* sched_flag;  // set if such a wait gave up
 };
 
 constexpr int kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own L2
@@ -91,6 +97,13 @@ __device__ __forceinline__ void barrier_only() {
 // the compiler does not see them: their waits are counted by hand.
 __device__ __forceinline__ void dma16(const void* base, uint32_t lane_off, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
+                    "s"(uniform_ptr(base)) : "memory");
+}
+// The same load, device-coherent (sc1): it reads data that another
+// workgroup of the same launch wrote with device-coherent stores.
+__device__ __forceinline__ void dma16_coh(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1"
                  :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
                     "s"(uniform_ptr(base)) : "memory");
 }

@@ -115,6 +115,8 @@ struct Item {
     int r0, rows, n0;
     int mia;                 // 32-row sub-tiles that hold rows: min(MI, ceil(rows / 32))
     int chunk, tile;         // K chunk of the item (split K) and its tile's counter index
+    int vb;                  // schedule block
+    bool down;               // a down item (the one-launch FFN only)
     const char* a_base;      // A rows: + kt * 128
     uint32_t a_off[MI];      // row byte offset + swizzled chunk
     const char* w_base;      // packed weights (W4), or the wavefront's bf16 matrix: + kt * 128
@@ -127,15 +129,17 @@ struct Item {
 // N_DMA = n_a + 3 loads in all.
 // The unfused twin (W4 = false) loads the wavefront's 64 bf16 weight rows
 // instead: 8 loads of 8 rows. N_DMA = n_a + 8.
-template <int BM, bool W4 = true>
+template <int BM, bool W4 = true, bool COH = false>
 __device__ __forceinline__ void issue_stage(const Item<BM / 32, W4>& it, int n_a, int kt, int buf,
                                             uint32_t smem, uint32_t wave, int lane) {
     using Ld = Lds<BM, W4>;
 #pragma unroll
     for (int j = 0; j < BM / 32; ++j)
-        if (j < n_a)
-            dma16(it.a_base + kt * 128, it.a_off[j],
-                  smem + Ld::A_OFF + buf * Ld::A + (32 * j + 8 * wave) * 128);
+        if (j < n_a) {
+            const uint32_t dst = smem + Ld::A_OFF + buf * Ld::A + (32 * j + 8 * wave) * 128;
+            if constexpr (COH) dma16_coh(it.a_base + kt * 128, it.a_off[j], dst);
+            else dma16(it.a_base + kt * 128, it.a_off[j], dst);
+        }
     if constexpr (!W4) {
         const uint32_t b_lds = smem + Ld::Q_OFF + buf * Ld::Q + 64u * wave * 128u;
 #pragma unroll
@@ -153,10 +157,27 @@ __device__ __forceinline__ void issue_stage(const Item<BM / 32, W4>& it, int n_a
     dma4(blk, sb_off, sb_lds);
 }
 
+// Waits (bounded) until the gate/up tiles of block vb have all stored
+// their h rows; a wait that gives up sets sched[30].
+__device__ __forceinline__ void wait_block_done(const GemmArgs& args, int vb) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(args.blk_done + vb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           args.blk_need) {
+        __builtin_amdgcn_s_sleep(2);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 50000000ull) {  // 0.5 s at 100 MHz
+            __hip_atomic_store(args.sched_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+}
+
 // Loads, multiplies and stores one tile. `prep_next` runs between the
 // k-loop and the stores: it takes and resolves the workgroup's next item, so
 // that the latency of its metadata loads overlaps the stores.
-template <int BM, bool GATED, int MIA, bool W4, typename PrepNext>
+// FUSED (the one-launch FFN): a gate/up tile stores h device-coherently and
+// then counts itself in blk_done; a down tile waits for that count before
+// its first loads and reads h device-coherently.
+template <int BM, bool GATED, int MIA, bool W4, bool FUSED, typename PrepNext>
 __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
                                           const Item<BM / 32, W4>& lp, uint32_t wave, int* s_flag,
                                           PrepNext&& prep_next) {
@@ -178,7 +199,9 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         col0[g] = GATED ? lp.n0 + 32 * (int)wave : lp.n0 + 64 * (int)wave + 32 * g;
     }
 
-    auto issue = [&](int kt, int buf) { issue_stage<BM, W4>(lp, MIA, kt, buf, smem, wave, lane); };
+    auto issue = [&](int kt, int buf) {
+        issue_stage<BM, W4, FUSED && !GATED>(lp, MIA, kt, buf, smem, wave, lane);
+    };
 
     f32x16 acc[MIA][NI];
 #pragma unroll
@@ -341,6 +364,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
     };
 
     if (!lp.prefetched) {
+        if constexpr (FUSED && !GATED) wait_block_done(args, lp.vb);
         issue(0, 0);
         if (NS == 3 && nk > 1) issue(1, 1);
     }
@@ -428,8 +452,13 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
                 float v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = silu(acc[i][0][4 * q + j]) * acc[i][1][4 * q + j];
-                *reinterpret_cast<u32x2*>(args.h_out + orow + col0[0] + 8 * q + 4 * h) =
-                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                uint16_t* dst = args.h_out + orow + col0[0] + 8 * q + 4 * h;
+                const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+                if constexpr (FUSED)
+                    __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), (uint64_t)lo | ((uint64_t)hi << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
             } else {
 #pragma unroll
                 for (int g = 0; g < NI; ++g)
@@ -439,6 +468,81 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
             }
         }
     }
+    if constexpr (FUSED && GATED) {
+        // Every wavefront's h stores have reached the device-coherent level
+        // before the tile counts itself in its block's tally.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier_only();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(args.blk_done + lp.vb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Resolves the rows, expert and load plan of tile (vb, nt), K chunk `chunk`,
+// of one GEMM for this wavefront (one load of block_info).
+template <int BM, bool GATED, bool W4>
+__device__ __forceinline__ void resolve_item(const GemmArgs& args, int vb, int nt, int chunk,
+                                             uint32_t wave, int lane, Item<BM / 32, W4>& it) {
+    constexpr int BN = GemmShape<GATED>::BN;
+    constexpr int MI = BM / 32;
+    const int n_tiles = args.N / BN;
+    const int n_slabs = args.N / kPackRows;
+    const size_t slab_bytes = (size_t)(args.K / 64) * kPackBlock;
+    it.chunk = chunk;
+    it.vb = vb;
+    it.tile = vb * n_tiles + nt;
+    int e = 0;
+    bool shared;
+    if (vb < args.shared_blocks) {
+        it.r0 = args.P + vb * BM;
+        it.rows = min(BM, args.P + args.T - it.r0);
+        shared = true;
+    } else {
+        const int4 info = args.block_info[vb - args.shared_blocks];
+        e = info.x;
+        it.r0 = info.y;
+        it.rows = info.z;
+        shared = false;
+    }
+    it.mia = min(MI, (it.rows + 31) / 32);
+    it.prefetched = false;
+    it.n0 = nt * BN;
+    // A loads: load j of wavefront w fills LDS rows 32j + 8w + lane/8,
+    // physical chunk lane%8, which holds logical chunk swz(row, lane%8).
+    // Rows past the block read the block's first row: their products land
+    // in output rows that are never stored.
+    const int kt0 = chunk * (args.K / 64 / args.kc);  // first k-step of the chunk
+    it.a_base = reinterpret_cast<const char*>(args.a) + kt0 * 128;
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+        const int row = 32 * j + 8 * (int)wave + lane / 8;
+        const int r = it.r0 + (row < it.rows ? row : 0);
+        int src_row = r;
+        if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
+        it.a_off[j] = (uint32_t)src_row * (uint32_t)(args.K * 2) + (uint32_t)(swz(row, lane % 8) * 16);
+    }
+    // Weight slab wb = wave / 2 of the workgroup: gate/up -> slab nt of the
+    // gate (wb = 0) or up (wb = 1) stack; down -> slab 2 nt + wb.
+    const int wb = (int)(wave >> 1);
+    const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
+    if constexpr (W4) {
+        const int slab = GATED ? nt : 2 * nt + wb;
+        it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes + (size_t)kt0 * kPackBlock;
+    } else {
+        // bf16 [n][N][K] stacks: the wavefront loads the workgroup's weight
+        // rows 64 w .. 64 w + 63 (LDS rows, swizzled like A): gate/up -> row
+        // n0 + (64 w + i) % 128 of the gate or up matrix; down -> row
+        // n0 + 64 w + i.
+        it.w_base = stack + (size_t)e * args.N * args.K * 2 + (size_t)kt0 * 128;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int lrow = 64 * (int)wave + 8 * j + lane / 8;
+            const int n = it.n0 + (GATED ? lrow % 128 : lrow);
+            it.b_off[j] = (uint32_t)n * (uint32_t)(args.K * 2) + (uint32_t)(swz(lrow, lane % 8) * 16);
+        }
+    }
+    it.down = !GATED;
+    it.valid = true;
 }
 
 template <int BM, bool GATED, bool W4 = true>
@@ -462,8 +566,6 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
     // for the last counters.)
     const int n_tiles = args.N / BN;
     const int nb_total = args.shared_blocks + args.num_blocks[0];
-    const int n_slabs = args.N / kPackRows;
-    const size_t slab_bytes = (size_t)(args.K / 64) * kPackBlock;
     const int cq = blockIdx.x % kXcds;
     int toggle = 0;
 
@@ -478,69 +580,9 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
         it.valid = false;
         const int c = grab(args.sched + cq, s_slot, toggle);
         if (c >= items_of(cq)) return;
-        {
-            const int ct = c / args.kc;  // tile of the queue
-            it.chunk = c - ct * args.kc;
-            const int qi = ct / n_tiles;  // block of the queue
-            const int vb = queue_block(cq, qi);
-            const int nt = ct % n_tiles;
-            it.tile = vb * n_tiles + nt;
-            int e = 0;
-            bool shared;
-            if (vb < args.shared_blocks) {
-                it.r0 = args.P + vb * BM;
-                it.rows = min(BM, args.P + args.T - it.r0);
-                shared = true;
-            } else {
-                const int4 info = args.block_info[vb - args.shared_blocks];
-                e = info.x;
-                it.r0 = info.y;
-                it.rows = info.z;
-                shared = false;
-            }
-            it.mia = min(MI, (it.rows + 31) / 32);
-            it.prefetched = false;
-            it.n0 = nt * BN;
-            // A loads: load j of wavefront w fills LDS rows 32j + 8w +
-            // lane/8, physical chunk lane%8, which holds logical chunk
-            // swz(row, lane%8). Rows past the block read the block's first
-            // row: their products land in output rows that are never
-            // stored.
-            const int kt0 = it.chunk * (args.K / 64 / args.kc);  // first k-step of the chunk
-            it.a_base = reinterpret_cast<const char*>(args.a) + kt0 * 128;
-#pragma unroll
-            for (int j = 0; j < MI; ++j) {
-                const int row = 32 * j + 8 * (int)wave + lane / 8;
-                const int r = it.r0 + (row < it.rows ? row : 0);
-                int src_row = r;
-                if (GATED) src_row = (r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P;
-                it.a_off[j] = (uint32_t)src_row * (uint32_t)(args.K * 2) +
-                              (uint32_t)(swz(row, lane % 8) * 16);
-            }
-            // Weight slab wb = wave / 2 of the workgroup: gate/up -> slab
-            // nt of the gate (wb = 0) or up (wb = 1) stack; down -> slab
-            // 2 nt + wb.
-            const int wb = (int)(wave >> 1);
-            const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
-            if constexpr (W4) {
-                const int slab = GATED ? nt : 2 * nt + wb;
-                it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes + (size_t)kt0 * kPackBlock;
-            } else {
-                // bf16 [n][N][K] stacks: the wavefront loads the workgroup's
-                // weight rows 64 w .. 64 w + 63 (LDS rows, swizzled like A):
-                // gate/up -> row n0 + (64 w + i) % 128 of the gate or up
-                // matrix; down -> row n0 + 64 w + i.
-                it.w_base = stack + (size_t)e * args.N * args.K * 2 + (size_t)kt0 * 128;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int lrow = 64 * (int)wave + 8 * j + lane / 8;
-                    const int n = it.n0 + (GATED ? lrow % 128 : lrow);
-                    it.b_off[j] = (uint32_t)n * (uint32_t)(args.K * 2) + (uint32_t)(swz(lrow, lane % 8) * 16);
-                }
-            }
-            it.valid = true;
-            return;
-        }
+        const int ct = c / args.kc;  // tile of the queue
+        resolve_item<BM, GATED, W4>(args, queue_block(cq, ct / n_tiles), ct % n_tiles, c - ct * args.kc,
+                                    wave, lane, it);
     };
     // Every decision follows a value that grab() sent through LDS, so all
     // wavefronts take the same path and meet at the same barriers.
@@ -564,10 +606,11 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
         // Only the 32-row sub-tiles that hold rows of the block are loaded
         // and multiplied.
         const int mia = cur.mia;
-        if (mia >= MI) gemm_main<BM, GATED, MI, W4>(args, smem, cur, wave, s_slot + 2, prep);
-        else if (mia == 1) gemm_main<BM, GATED, 1, W4>(args, smem, cur, wave, s_slot + 2, prep);
-        else if (mia == 2) gemm_main<BM, GATED, (MI > 2 ? 2 : 1), W4>(args, smem, cur, wave, s_slot + 2, prep);
-        else gemm_main<BM, GATED, (MI > 3 ? 3 : 1), W4>(args, smem, cur, wave, s_slot + 2, prep);
+        if (mia >= MI) gemm_main<BM, GATED, MI, W4, false>(args, smem, cur, wave, s_slot + 2, prep);
+        else if (mia == 1) gemm_main<BM, GATED, 1, W4, false>(args, smem, cur, wave, s_slot + 2, prep);
+        else if (mia == 2)
+            gemm_main<BM, GATED, (MI > 2 ? 2 : 1), W4, false>(args, smem, cur, wave, s_slot + 2, prep);
+        else gemm_main<BM, GATED, (MI > 3 ? 3 : 1), W4, false>(args, smem, cur, wave, s_slot + 2, prep);
         cur = nxt;
     }
 
@@ -576,6 +619,91 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
     // next launch.
     if (tid == 0 && atomicAdd(args.sched + kXcds, 1) == (int)gridDim.x - 1) {
         for (int i = 0; i <= kXcds; ++i) atomicExch(args.sched + i, 0);
+    }
+}
+
+// Gate/up and down in one launch (no split K). Queue q takes its gate/up
+// items, then its down items (the same blocks, dealt the same way), from
+// one counter, so a workgroup whose gate/up work has run out starts on down
+// tiles while the last gate/up tiles finish elsewhere, instead of idling
+// until a second launch. A down item waits until its block's gate/up tiles
+// have counted in; they were all taken before it from the same counter, by
+// workgroups that are running and wait on nothing, so the wait ends. Those
+// h rows are stored and read device-coherently, because producer and
+// consumer may sit on different XCDs (each with its own L2).
+template <int BM>
+__global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD)
+    moe_w4_ffn(GemmArgs gu, GemmArgs dn) {
+    constexpr int MI = BM / 32;
+    constexpr int NS = Lds<BM, true>::NS;
+    __shared__ __attribute__((aligned(16))) char smem[Lds<BM, true>::TOTAL];
+    __shared__ int s_slot[3];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nb_total = gu.shared_blocks + gu.num_blocks[0];
+    const int nt_gu = gu.N / GemmShape<true>::BN, nt_dn = dn.N / GemmShape<false>::BN;
+    const int cq = blockIdx.x % kXcds;
+    const int n_gu = queue_items(nb_total, cq, nt_gu);
+    const int n_dn = queue_items(nb_total, cq, nt_dn);
+    int toggle = 0;
+    auto take = [&](Item<MI, true>& it) {
+        it.valid = false;
+        int c = grab(gu.sched + cq, s_slot, toggle);
+        if (c < n_gu) {
+            resolve_item<BM, true, true>(gu, queue_block(cq, c / nt_gu), c % nt_gu, 0, wave, lane, it);
+        } else if ((c -= n_gu) < n_dn) {
+            resolve_item<BM, false, true>(dn, queue_block(cq, c / nt_dn), c % nt_dn, 0, wave, lane, it);
+        }
+    };
+    const uint32_t smem_addr = (uint32_t)(size_t)smem;
+    Item<MI, true> cur;
+    take(cur);
+    while (cur.valid) {
+        Item<MI, true> nxt;
+        // As in the separate launches; a down item's first stages are
+        // prefetched only if its block is already complete.
+        auto prep = [&]() {
+            take(nxt);
+            if (nxt.valid &&
+                (!nxt.down || __hip_atomic_load(dn.blk_done + nxt.vb, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) >= dn.blk_need)) {
+#pragma unroll
+                for (int u = 0; u < NS - 1; ++u) {
+                    if (u >= gu.K / 64 && !nxt.down) continue;
+                    if (u >= dn.K / 64 && nxt.down) continue;
+                    if (nxt.down) issue_stage<BM, true, true>(nxt, nxt.mia, u, u, smem_addr, wave, lane);
+                    else issue_stage<BM, true, false>(nxt, nxt.mia, u, u, smem_addr, wave, lane);
+                }
+                nxt.prefetched = true;
+            }
+        };
+        const int mia = cur.mia;
+        if (!cur.down) {
+            if (mia >= MI) gemm_main<BM, true, MI, true, true>(gu, smem, cur, wave, s_slot + 2, prep);
+            else if (mia == 1) gemm_main<BM, true, 1, true, true>(gu, smem, cur, wave, s_slot + 2, prep);
+            else if (mia == 2)
+                gemm_main<BM, true, (MI > 2 ? 2 : 1), true, true>(gu, smem, cur, wave, s_slot + 2, prep);
+            else gemm_main<BM, true, (MI > 3 ? 3 : 1), true, true>(gu, smem, cur, wave, s_slot + 2, prep);
+        } else {
+            if (mia >= MI) gemm_main<BM, false, MI, true, true>(dn, smem, cur, wave, s_slot + 2, prep);
+            else if (mia == 1) gemm_main<BM, false, 1, true, true>(dn, smem, cur, wave, s_slot + 2, prep);
+            else if (mia == 2)
+                gemm_main<BM, false, (MI > 2 ? 2 : 1), true, true>(dn, smem, cur, wave, s_slot + 2, prep);
+            else gemm_main<BM, false, (MI > 3 ? 3 : 1), true, true>(dn, smem, cur, wave, s_slot + 2, prep);
+        }
+        cur = nxt;
+    }
+
+    // The last workgroup to get here (every item taken and finished) clears
+    // the queue counters and the block tallies for the next launch.
+    if (tid == 0) s_slot[2] = atomicAdd(gu.sched + kXcds, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (s_slot[2]) {
+        for (int i = tid; i < nb_total; i += kGemmThreads)
+            __hip_atomic_store(gu.blk_done + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid <= kXcds) atomicExch(gu.sched + tid, 0);
     }
 }
 
@@ -777,11 +905,8 @@ static int launch_down_bm(GemmArgs g, int max_blocks, hipStream_t stream) {
     return check_launch("down_gemm");
 }
 
-// G1 + G2 (and the shared expert's rows): h = bf16(silu(x Wg^T) * (x Wu^T)).
-// w4 = false: the unfused twin, whose weights are bf16 [n][N][K] stacks.
-int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
-                   const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
-                   hipStream_t stream, bool w4) {
+static GemmArgs gate_up_args(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+                             const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws) {
     GemmArgs g = routing_args(d, r);
     g.a = x;
     g.sorted_pairs = r.sorted_pairs;
@@ -796,6 +921,31 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
     g.kc = split_k(d, max_blocks, true);
     g.part = ws.part;
     g.tile_ctr = r.sched + kQueueInts;
+    return g;
+}
+
+static GemmArgs down_args(const lily_moe_dims& d, const lily_moe_weights& w, const lily_moe_routing& r,
+                          int max_blocks, const ForwardWorkspace& ws) {
+    GemmArgs g = routing_args(d, r);
+    g.a = ws.h;
+    g.w[0] = g.w[1] = static_cast<const char*>(w.down);
+    g.sw[0] = g.sw[1] = static_cast<const char*>(w.sh_down);
+    g.N = d.H;
+    g.K = d.F;
+    g.sched = r.sched + kQueueInts / 2;
+    g.y_out = ws.y;
+    g.kc = split_k(d, max_blocks, false);
+    g.part = ws.part;
+    g.tile_ctr = r.sched + kQueueInts + kTileCounters;
+    return g;
+}
+
+// G1 + G2 (and the shared expert's rows): h = bf16(silu(x Wg^T) * (x Wu^T)).
+// w4 = false: the unfused twin, whose weights are bf16 [n][N][K] stacks.
+int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+                   const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
+                   hipStream_t stream, bool w4) {
+    GemmArgs g = gate_up_args(d, w, x, r, max_blocks, ws);
     if (!w4) {
         if (d.tile_m == 32) return launch_gate_up_bm<32, false>(g, max_blocks, stream);
         if (d.tile_m == 64) return launch_gate_up_bm<64, false>(g, max_blocks, stream);
@@ -812,17 +962,7 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
 // G3 (and the shared expert's rows): y = h Wd^T in fp32.
 int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_moe_routing& r,
                 int max_blocks, const ForwardWorkspace& ws, hipStream_t stream, bool w4) {
-    GemmArgs g = routing_args(d, r);
-    g.a = ws.h;
-    g.w[0] = g.w[1] = static_cast<const char*>(w.down);
-    g.sw[0] = g.sw[1] = static_cast<const char*>(w.sh_down);
-    g.N = d.H;
-    g.K = d.F;
-    g.sched = r.sched + kQueueInts / 2;
-    g.y_out = ws.y;
-    g.kc = split_k(d, max_blocks, false);
-    g.part = ws.part;
-    g.tile_ctr = r.sched + kQueueInts + kTileCounters;
+    GemmArgs g = down_args(d, w, r, max_blocks, ws);
     if (!w4) {
         if (d.tile_m == 32) return launch_down_bm<32, false>(g, max_blocks, stream);
         if (d.tile_m == 64) return launch_down_bm<64, false>(g, max_blocks, stream);
@@ -834,6 +974,57 @@ int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_mo
         case 128: return launch_down_bm<128, true>(g, max_blocks, stream);
     }
     return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d not supported", d.tile_m);
+}
+
+template <int BM>
+static int launch_ffn_bm(GemmArgs gu, GemmArgs dn, int max_blocks, hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static int resident[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int slots = dev < kMaxDevices ? resident[dev] : 0;
+    if (slots == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_w4_ffn<BM>, kGemmThreads, 0) !=
+            hipSuccess)
+            per_cu = 0;
+        slots = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+        if (dev < kMaxDevices) resident[dev] = slots;
+    }
+    const long items = (long)(max_blocks + gu.shared_blocks) *
+                       (gu.N / GemmShape<true>::BN + dn.N / GemmShape<false>::BN);
+    const long grid = items < slots ? items : slots;
+    hipLaunchKernelGGL(moe_w4_ffn<BM>, dim3((unsigned)((grid + kXcds - 1) / kXcds * kXcds)),
+                       dim3(kGemmThreads), 0, stream, gu, dn);
+    return check_launch("ffn_gemms");
+}
+
+// G1-G3 in one launch (moe_w4_ffn) when neither GEMM splits K and the
+// schedule's blocks fit the block tallies (which take the split-K tile
+// counters of both GEMMs, unused then). Returns 1, having launched
+// nothing, when it does not apply.
+int launch_ffn(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
+               const lily_moe_routing& r, int max_blocks, const ForwardWorkspace& ws,
+               hipStream_t stream) {
+    GemmArgs gu = gate_up_args(d, w, x, r, max_blocks, ws);
+    GemmArgs dn = down_args(d, w, r, max_blocks, ws);
+    const int shared_blocks = (d.T + d.tile_m - 1) / d.tile_m;
+    if (gu.kc != 1 || dn.kc != 1 || (long)max_blocks + shared_blocks > 2L * kTileCounters ||
+        d.F % GemmShape<true>::BN != 0)
+        return 1;
+    gu.shared_blocks = dn.shared_blocks = shared_blocks;
+    gu.blk_done = dn.blk_done = r.sched + kQueueInts;
+    gu.blk_need = dn.blk_need = d.F / GemmShape<true>::BN;
+    gu.sched_flag = dn.sched_flag = r.sched + kDecodeBarrier + 2;
+    dn.sched = gu.sched;
+    switch (d.tile_m) {
+        case 32: return launch_ffn_bm<32>(gu, dn, max_blocks, stream);
+        case 64: return launch_ffn_bm<64>(gu, dn, max_blocks, stream);
+        case 128: return launch_ffn_bm<128>(gu, dn, max_blocks, stream);
+    }
+    return 1;
 }
 
 size_t packed_w4_bytes(int n, int N, int K) {

@@ -292,6 +292,36 @@ def test_gemm_queue_counters_reset():
     assert not np.any(r.sched.cpu().numpy())
 
 
+@pytest.mark.parametrize("name,tile_m", [("prefill2048_zipf", 128), ("prefill512", 128),
+                                         ("prefill512", 64), ("prefill2048_zipf", 32), ("tiny", 32)])
+def test_ffn_one_launch(name, tile_m):
+    """lily_moe_ffn (gate/up and down in one launch where neither splits K,
+    a down tile waiting for its block's gate/up tiles) writes the same h and y
+    bit for bit as lily_moe_gate_up then lily_moe_down, three times in a row
+    on one routing (its queue counters and block tallies are left zero, and
+    no wait gave up)."""
+    cfg = S.CONFIGS[name]
+    _flush(f"one-launch ffn {name} tile_m={tile_m}")
+    d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, tile_m)
+    w = L.weights_from_host(S.layer_weights(cfg, 0))
+    xd = G.to_dev_bits(S.activations(cfg))
+    r = G.route_gpu(d, S.router_logits(cfg))
+    ws = L.alloc_workspace(d)
+    h, y = L.workspace_views(d, ws)
+    L.lily_moe_gate_up(d, w, xd, r, ws)
+    L.lily_moe_down(d, w, r, ws)
+    torch.cuda.synchronize()
+    want_h, want_y = h.clone(), y.clone()
+    for _ in range(3):
+        h.fill_(0)
+        y.fill_(0)
+        L.lily_moe_ffn(d, w, xd, r, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(h, want_h), "h differs from the two launches"
+        assert torch.equal(y, want_y), "y differs from the two launches"
+        assert not np.any(r.sched.cpu().numpy()), "counters, tallies and the give-up flag stay zero"
+
+
 # ------------------------------------------------------------------- split K
 
 @pytest.mark.parametrize("T,tile_m", [(1, 32), (1, 128), (4, 32), (8, 64), (3, 128)])
