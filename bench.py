@@ -175,6 +175,18 @@ def main():
     return main_prefill(args)
 
 
+def copy_calibration(dev):
+    """Two plain device copies of 256 MiB after the timed region: the
+    reference that FETCH_SIZE / WRITE_SIZE counter passes are scaled by."""
+    import torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main_prefill(args):
     import numpy as np
     import torch
@@ -253,12 +265,7 @@ def main_prefill(args):
     t1 = time.perf_counter()
 
     if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = cfg.T / ((t1 - t0) / args.steps)
@@ -463,6 +470,8 @@ def run_decode(args, n_layers_distinct, steps, warmup, path, brief=False):
         step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if getattr(args, "copy_calibration", False) and not brief:
+        copy_calibration(dev)
     if path != "layer" and int(routing.sched[30].item()) != 0:
         print("decode: a device-wide barrier wait gave up (sched[30] set): the workgroups "
               "were not all resident, outputs and timing are invalid", file=sys.stderr)
