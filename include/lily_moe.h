@@ -55,8 +55,8 @@ extern "C" {
 
 /* Layer sizes. T tokens, hidden size H, expert FFN size F, E routed experts,
    topk experts per token, group = 64 (the only supported group), tile_m =
-   rows per block of the block map (32, 64 or 128 for lily_moe_forward; any
-   value >= 1 for lily_moe_route). H and F must be multiples of 64;
+   rows per block of the block map (16, 32, 64 or 128 for lily_moe_forward;
+   any value >= 1 for lily_moe_route). H and F must be multiples of 64;
    1 <= topk <= E <= 512; T >= 1. */
 typedef struct {
     int32_t T, H, F, E, topk, group, tile_m;
@@ -230,7 +230,7 @@ int lily_moe_route_host(const lily_moe_dims* dims, const float* logits,
    lily_moe_workspace_bytes(dims) bytes of device memory (contents on entry
    are ignored). The routing is trusted (ids in range, block map as produced
    by lily_moe_route). Run-to-run deterministic: no floating-point atomics.
-   Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (tile_m not 32/64/128,
+   Errors: LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (tile_m not 16/32/64/128,
    H not a multiple of 256, F not a multiple of 128, or x [T, H], h
    [T * (topk + 1), F] or one [F, H] matrix as bf16 reaching 4 GiB: the
    kernels address rows with 32-bit byte offsets), LILY_ERR_WORKSPACE,

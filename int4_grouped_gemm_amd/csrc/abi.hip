@@ -144,8 +144,8 @@ static int check_forward_args(const lily_moe_dims* dims, const lily_moe_weights*
         return rc;
     rc = check_routing(routing);
     if (rc) return rc;
-    if (dims->tile_m != 32 && dims->tile_m != 64 && dims->tile_m != 128)
-        return set_error(LILY_ERR_UNSUPPORTED, "tile_m = %d; forward supports 32, 64, 128",
+    if (dims->tile_m != 16 && dims->tile_m != 32 && dims->tile_m != 64 && dims->tile_m != 128)
+        return set_error(LILY_ERR_UNSUPPORTED, "tile_m = %d; forward supports 16, 32, 64, 128",
                          dims->tile_m);
     if (dims->H % 256)
         return set_error(LILY_ERR_UNSUPPORTED, "H = %d must be a multiple of 256", dims->H);

@@ -707,6 +707,218 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD)
     }
 }
 
+// 16-row tiles (tile_m 16): the tile height the Lily articles start from
+// (news.ainew.jp Lily article, section "Prefill", 16 against 32 rows per
+// threadgroup tile). A block of <= 16 rows against the same 256 weight rows
+// of two packed slabs as the taller tiles, on v_mfma_f32_16x16x32_bf16:
+// the weights are the first operand (16 rows x 32 k), the block's rows the
+// second. A wavefront holds 16 accumulators (4 groups of 16 weight rows x
+// 16 tokens), so four wavefronts fit per SIMD, which is what the
+// dequant-bound small blocks want; the dequantisation per k-step and
+// workgroup is the same 256 x 64 weights as in the taller tiles.
+//
+// K mapping inside a 64-wide k-step: MFMA m (0, 1) of lane quarter q =
+// lane / 16 takes k 16q + 8m .. 16q + 8m + 7, for both operands. So a lane
+// reads 8 bytes of int4 per weight row (k 16q .. 16q + 15, one ds_read_b64
+// from half q / 2 of the packed row) and 16-byte A chunks 2q and 2q + 1.
+// Weight groups of wavefront w: gate/up -> gate rows 32w, 32w + 16 and the
+// same up rows (SwiGLU local to a lane); down -> rows 64w + 16g.
+struct Lds16 {
+    static constexpr int NS = 3;
+    static constexpr int Q = 256 * 32;
+    static constexpr int SB = 256 * 2 * 2;
+    static constexpr int A = 16 * 128;
+    static constexpr int Q_OFF = 0;
+    static constexpr int SB_OFF = Q_OFF + NS * Q;
+    static constexpr int A_OFF = SB_OFF + NS * SB;
+    static constexpr int TOTAL = NS * (A + Q + SB);
+};
+
+struct Item16 {
+    bool valid;
+    bool prefetched;
+    int r0, rows, n0;
+    const char* a_base;  // + kt * 128
+    uint32_t a_off;      // this lane's A row byte offset + swizzled chunk (lanes 0-31)
+    const char* w_base;  // + kt * kPackBlock
+};
+
+// One k-step stage by one wavefront: A rows 4w .. 4w + 3 (lanes 0-31), then
+// its share of the weight slabs and scales as in issue_stage. 4 loads.
+__device__ __forceinline__ void issue_stage16(const Item16& it, int kt, int buf, uint32_t smem,
+                                              uint32_t wave, int lane) {
+    if (lane < 32)
+        dma16(it.a_base + kt * 128, it.a_off, smem + Lds16::A_OFF + buf * Lds16::A + 4 * wave * 128);
+    const uint32_t wh = wave & 1u, wb = wave >> 1;
+    const uint32_t q_off = (wh * 128u + (uint32_t)lane) * 16u;
+    const uint32_t sb_off = (uint32_t)kPackQ + wh * 256u + (uint32_t)lane * 4u;
+    const uint32_t q_lds = smem + Lds16::Q_OFF + buf * Lds16::Q + (wh * 256u + wb * 128u) * 16u;
+    const uint32_t sb_lds = smem + Lds16::SB_OFF + buf * Lds16::SB + wh * 512u + wb * 256u;
+    const char* blk = it.w_base + (size_t)kt * kPackBlock;
+    dma16(blk, q_off, q_lds);
+    dma16(blk, q_off + 64 * 16, q_lds + 64 * 16);
+    dma4(blk, sb_off, sb_lds);
+}
+
+template <bool GATED>
+__global__ void __launch_bounds__(kGemmThreads, 4) moe_w4_gemm16(GemmArgs args) {
+    constexpr int BN = GemmShape<GATED>::BN;
+    constexpr int NS = Lds16::NS;
+    constexpr int N_DMA = 4;
+    __shared__ __attribute__((aligned(16))) char smem[Lds16::TOTAL];
+    __shared__ int s_slot[2];
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int q = lane / 16, x = lane % 16;
+    const int n_tiles = args.N / BN;
+    const int n_slabs = args.N / kPackRows;
+    const size_t slab_bytes = (size_t)(args.K / 64) * kPackBlock;
+    const int nb_total = args.shared_blocks + args.num_blocks[0];
+    const int nk = args.K / 64;
+    const int cq = blockIdx.x % kXcds;
+    const int n_items = queue_items(nb_total, cq, n_tiles);
+    int toggle = 0;
+
+    auto take = [&](Item16& it) {
+        it.valid = false;
+        const int c = grab(args.sched + cq, s_slot, toggle);
+        if (c >= n_items) return;
+        const int vb = queue_block(cq, c / n_tiles), nt = c % n_tiles;
+        int e = 0;
+        bool shared;
+        if (vb < args.shared_blocks) {
+            it.r0 = args.P + vb * 16;
+            it.rows = min(16, args.P + args.T - it.r0);
+            shared = true;
+        } else {
+            const int4 info = args.block_info[vb - args.shared_blocks];
+            e = info.x;
+            it.r0 = info.y;
+            it.rows = info.z;
+            shared = false;
+        }
+        it.n0 = nt * BN;
+        it.prefetched = false;
+        it.a_base = reinterpret_cast<const char*>(args.a);
+        // lanes 0-31 load LDS rows 4w + lane / 8, physical chunk lane % 8
+        // (logical chunk swz(row, lane % 8)); rows past the block read its
+        // first row, whose products land in outputs that are never stored
+        const int row = 4 * (int)wave + (lane % 32) / 8;
+        const int r = it.r0 + (row < it.rows ? row : 0);
+        const int src_row = GATED ? ((r < args.P) ? args.sorted_pairs[r] / args.topk : r - args.P) : r;
+        it.a_off = (uint32_t)src_row * (uint32_t)(args.K * 2) + (uint32_t)(swz(row, lane % 8) * 16);
+        const int wb = (int)(wave >> 1);
+        const char* stack = shared ? args.sw[GATED ? wb : 0] : args.w[GATED ? wb : 0];
+        const int slab = GATED ? nt : 2 * nt + wb;
+        it.w_base = stack + ((size_t)e * n_slabs + slab) * slab_bytes;
+        it.valid = true;
+    };
+
+    // Per-lane LDS read offsets inside a stage.
+    uint32_t a_rd[2], q_rd[4], sb_rd[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) a_rd[m] = x * 128 + swz(x, 2 * q + m) * 16;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int qrow = GATED ? (g < 2 ? 32 * (int)wave + 16 * g : 128 + 32 * (int)wave + 16 * (g - 2)) + x
+                               : 64 * (int)wave + 16 * g + x;
+        q_rd[g] = ((q / 2) * 256 + qrow) * 16 + (q % 2) * 8;
+        sb_rd[g] = qrow * 2;
+    }
+
+    const uint32_t smem_addr = (uint32_t)(size_t)smem;
+    Item16 cur;
+    take(cur);
+    while (cur.valid) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (!cur.prefetched) {
+#pragma unroll
+            for (int u = 0; u < NS - 1; ++u)
+                if (u < nk) issue_stage16(cur, u, u, smem_addr, wave, lane);
+        }
+        auto step = [&](int kt, int buf) {
+            if (kt + 1 >= nk) wait_vmcnt<0>();
+            else wait_vmcnt<N_DMA>();
+            barrier_only();
+            if (kt + NS - 1 < nk) issue_stage16(cur, kt + NS - 1, (buf + NS - 1) % NS, smem_addr, wave, lane);
+            const char* Ab = smem + Lds16::A_OFF + buf * Lds16::A;
+            const char* Qb = smem + Lds16::Q_OFF + buf * Lds16::Q;
+            const char* Sb = smem + Lds16::SB_OFF + buf * Lds16::SB;
+            u32x2 qw[4];
+            float s512[4], bias[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                qw[g] = *reinterpret_cast<const u32x2*>(Qb + q_rd[g]);
+                s512[g] = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + sb_rd[g])) * 512.0f;
+                bias[g] = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(Sb + 512 + sb_rd[g]));
+            }
+            bf16x8 af[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) af[m] = *reinterpret_cast<const bf16x8*>(Ab + a_rd[m]);
+            bf16x8 bw[4][2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    uint32_t w[4];
+                    dequant8(qw[g][m], s512[g], bias[g], w);
+                    bw[g][m] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+                }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[g][m], af[m], acc[g], 0, 0, 0);
+            wait_lgkmcnt0();
+        };
+        int kt = 0;
+        for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) step(kt + u, u);
+        }
+#pragma unroll
+        for (int u = 0; u < NS - 1; ++u)
+            if (kt + u < nk) step(kt + u, u);
+
+        // next item and its first stages, overlapping the stores below
+        Item16 nxt;
+        take(nxt);
+        if (nxt.valid) {
+#pragma unroll
+            for (int u = 0; u < NS - 1; ++u)
+                if (u < nk) issue_stage16(nxt, u, u, smem_addr, wave, lane);
+            nxt.prefetched = true;
+        }
+        // Lane l, register r of group g holds weight row 4 (l / 16) + r of
+        // the group for token l % 16: four consecutive output columns.
+        if (x < cur.rows) {
+            const size_t orow = (size_t)(cur.r0 + x) * args.N;
+            if (GATED) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = silu(acc[g][j]) * acc[g + 2][j];
+                    *reinterpret_cast<u32x2*>(args.h_out + orow + cur.n0 + 32 * (int)wave + 16 * g + 4 * q) =
+                        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4*>(args.y_out + orow + cur.n0 + 64 * (int)wave + 16 * g + 4 * q) =
+                        acc[g];
+            }
+        }
+        cur = nxt;
+    }
+    if (tid == 0 && atomicAdd(args.sched + kXcds, 1) == (int)gridDim.x - 1) {
+        for (int i = 0; i <= kXcds; ++i) atomicExch(args.sched + i, 0);
+    }
+}
+
 // One thread per (expert, row, group): the row's 32 q bytes of the group go
 // to the two halves of its packed block, the scale and bias behind them.
 __global__ void __launch_bounds__(256) pack_w4_kernel(const uint8_t* __restrict__ q,
@@ -817,6 +1029,7 @@ constexpr int kSplitMinSteps = 4;
 static_assert(kSplitItems / 2 <= kTileCounters, "split-K tile counters");
 
 static int split_k(const lily_moe_dims& d, int max_blocks, bool gated) {
+    if (d.tile_m == 16) return 1;  // the 16-row tiles do not split K
     const int BN = gated ? 128 : 256;
     const int N = gated ? d.F : d.H;
     const int nk = (gated ? d.H : d.F) / 64;
@@ -940,6 +1153,31 @@ static GemmArgs down_args(const lily_moe_dims& d, const lily_moe_weights& w, con
     return g;
 }
 
+template <bool GATED>
+static int launch_gemm16(GemmArgs g, int max_blocks, hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static int resident[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int slots = dev < kMaxDevices ? resident[dev] : 0;
+    if (slots == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_w4_gemm16<GATED>, kGemmThreads,
+                                                         0) != hipSuccess)
+            per_cu = 0;
+        slots = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+        if (dev < kMaxDevices) resident[dev] = slots;
+    }
+    g.shared_blocks = (g.T + 15) / 16;
+    const long items = (long)(max_blocks + g.shared_blocks) * (g.N / GemmShape<GATED>::BN);
+    const long grid = items < slots ? items : slots;
+    hipLaunchKernelGGL(moe_w4_gemm16<GATED>, dim3((unsigned)((grid + kXcds - 1) / kXcds * kXcds)),
+                       dim3(kGemmThreads), 0, stream, g);
+    return check_launch(GATED ? "gate_up_gemm16" : "down_gemm16");
+}
+
 // G1 + G2 (and the shared expert's rows): h = bf16(silu(x Wg^T) * (x Wu^T)).
 // w4 = false: the unfused twin, whose weights are bf16 [n][N][K] stacks.
 int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t* x,
@@ -952,6 +1190,7 @@ int launch_gate_up(const lily_moe_dims& d, const lily_moe_weights& w, const uint
         return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d; the bf16 GEMMs take 32 or 64", d.tile_m);
     }
     switch (d.tile_m) {
+        case 16: return launch_gemm16<true>(g, max_blocks, stream);
         case 32: return launch_gate_up_bm<32, true>(g, max_blocks, stream);
         case 64: return launch_gate_up_bm<64, true>(g, max_blocks, stream);
         case 128: return launch_gate_up_bm<128, true>(g, max_blocks, stream);
@@ -969,6 +1208,7 @@ int launch_down(const lily_moe_dims& d, const lily_moe_weights& w, const lily_mo
         return set_error(LILY_ERR_UNSUPPORTED, "tile_m %d; the bf16 GEMMs take 32 or 64", d.tile_m);
     }
     switch (d.tile_m) {
+        case 16: return launch_gemm16<false>(g, max_blocks, stream);
         case 32: return launch_down_bm<32, true>(g, max_blocks, stream);
         case 64: return launch_down_bm<64, true>(g, max_blocks, stream);
         case 128: return launch_down_bm<128, true>(g, max_blocks, stream);

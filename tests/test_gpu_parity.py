@@ -196,7 +196,7 @@ def _layer_case(cfg, tile_m, tokens=None, layer=0, seed=0):
     return got, acc, (d, w, xd, r)
 
 
-@pytest.mark.parametrize("tile_m", [32, 64, 128])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
 def test_forward_tiny(tile_m):
     _flush(f"forward tiny tile_m={tile_m}")
     got, acc, _ = _layer_case(S.CONFIGS["tiny"], tile_m)
@@ -204,7 +204,7 @@ def test_forward_tiny(tile_m):
     assert err <= 1.0, f"normalised error {err}"
 
 
-@pytest.mark.parametrize("tile_m", [32, 64, 128])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
 def test_forward_prefill512(tile_m):
     _flush(f"forward prefill512 tile_m={tile_m}")
     got, acc, _ = _layer_case(S.CONFIGS["prefill512"], tile_m)
@@ -213,7 +213,7 @@ def test_forward_prefill512(tile_m):
     assert err <= 1.0, f"normalised error {err}"
 
 
-@pytest.mark.parametrize("tile_m", [64, 128])
+@pytest.mark.parametrize("tile_m", [16, 64, 128])
 def test_forward_zipf2048_all_tokens(tile_m):
     _flush(f"forward prefill2048_zipf, all tokens, tile_m={tile_m}")
     got, acc, (d, w, xd, r) = _layer_case(S.CONFIGS["prefill2048_zipf"], tile_m)
