@@ -128,7 +128,7 @@ typedef struct {
                               learns a block's extent with one load;
    sched int32 [LILY_SCHED_INTS]
                               work-queue and split-K tile counters of the
-                              grouped GEMMs (the first 1056 ints), then the
+                              grouped GEMMs (the first 1632 ints), then the
                               route's per-span expert histograms (64 rows of
                               512 counts and an arrival counter). Zero the
                               whole array once after allocating;
@@ -137,7 +137,7 @@ typedef struct {
                               leaves its counters zero when it completes.
                               Launches that share a routing buffer must be
                               ordered on one stream. */
-#define LILY_SCHED_INTS (1056 + 64 * 512 + 1)
+#define LILY_SCHED_INTS (1632 + 64 * 512 + 1)
 typedef struct {
     int32_t* topk_ids;
     float* topk_w;

@@ -32,7 +32,7 @@ EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_by
            "lily_last_error",
            # include/lily_calib.h
            "lily_calib_mfma", "lily_calib_read")
-LILY_SCHED_INTS = 1056 + 64 * 512 + 1
+LILY_SCHED_INTS = 1632 + 64 * 512 + 1
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
 

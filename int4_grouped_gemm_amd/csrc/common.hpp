@@ -12,14 +12,20 @@ constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kGroup = 64;     // weights per (scale, bias) group
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 64;
-// The routing's sched array: 16 queue/finish counters per GEMM (gate/up,
-// down), then the split-K tile counters of each GEMM (kCounterInts in
-// all), then the route's per-part expert histograms: kMaxParts rows of
-// kMaxExperts counts and one arrival counter.
+// The routing's sched array: kQueueInts words for the fused decode kernel's
+// barrier, then the split-K tile counters of each GEMM (kTileCounters per
+// GEMM), then each GEMM's queue counters and finished-workgroup counter
+// (kQueueCtrs, one per 128-byte line: counters that share a line serialise
+// their atomics; kCounterInts ints up to here), then the route's per-part
+// expert histograms: kMaxParts rows of kMaxExperts counts and one arrival
+// counter.
 constexpr int kSchedInts = LILY_SCHED_INTS;
 constexpr int kQueueInts = 32;
-constexpr int kCounterInts = 1056;
-constexpr int kTileCounters = (kCounterInts - kQueueInts) / 2;
+constexpr int kTileCounters = 512;
+constexpr int kQueueLine = 32;  // ints per 128-byte cache line
+constexpr int kQueueCtrs = 9;   // 8 XCD queues and the finished-workgroup count
+constexpr int kQueueBase = kQueueInts + 2 * kTileCounters;
+constexpr int kCounterInts = kQueueBase + 2 * kQueueCtrs * kQueueLine;
 constexpr int kMaxParts = 64;
 constexpr int kPartBase = kCounterInts;
 static_assert(kPartBase + kMaxParts * kMaxExperts + 1 == kSchedInts, "sched layout");

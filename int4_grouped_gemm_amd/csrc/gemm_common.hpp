@@ -19,7 +19,7 @@ struct GemmArgs {
     const int32_t* num_blocks;
     int shared_blocks;  // ceil(T / BM)
     int P, T;
-    int32_t* sched;     // kXcds queue counters, then the finished-workgroup counter
+    int32_t* sched;     // queue_ctr(sched, q): the kXcds queue counters and (q = kXcds) finished workgroups
     uint16_t* h_out;    // gate/up: h [P + T, N] bf16
     float* y_out;       // down: y [P + T, N] fp32
     // Split K (small block maps): each tile's K runs as kc items of K / kc;
@@ -38,7 +38,14 @@ struct GemmArgs {
 };
 
 constexpr int kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own L2
+static_assert(kQueueCtrs == kXcds + 1, "a counter per queue and the finished count");
 constexpr int kQueueChunk = 4;  // consecutive schedule blocks per queue turn
+
+// Counter q (< kXcds: a queue; kXcds: the finished workgroups) of a GEMM's
+// queue counters, each alone on its 128-byte line: every workgroup of a
+// launch takes its items with atomics on them, and atomics on one line
+// serialise (eight counters on one line cost a launch tens of microseconds).
+__device__ __forceinline__ int32_t* queue_ctr(int32_t* sched, int q) { return sched + q * kQueueLine; }
 
 // Output columns of one work item: the gate/up GEMM takes 128 features
 // (128 gate and the same 128 up weight rows, so that SwiGLU is local to a
@@ -49,20 +56,26 @@ struct GemmShape {
 };
 
 // The schedule (the shared expert's blocks, then the routed blocks in
-// block_order) is dealt to kXcds queues in turns of kQueueChunk consecutive
-// blocks: queue q owns blocks q*c .. q*c + c-1, (q + 8)*c .., ... (c =
-// kQueueChunk), so that most blocks of a hot expert meet its weight slabs
-// in one XCD's L2. Each block contributes n_tiles * kc consecutive items.
+// block_order) is dealt to kXcds queues in rounds of kXcds * kQueueChunk
+// blocks. In each full round queue q takes kQueueChunk consecutive blocks
+// (q*c .. q*c + c-1 of the round, c = kQueueChunk), so that most blocks of a
+// hot expert meet its weight slabs in one XCD's L2. The blocks after the
+// last full round (the smallest: block_order ends with the partial blocks)
+// go one at a time, q, q + 8, ..., so that the queues' block counts differ
+// by at most one (dealt in turns of c they differ by up to c, an eighth of
+// a launch's items at T = 2048). Each block contributes n_tiles * kc
+// consecutive items.
 __device__ __forceinline__ int queue_items(int nb_total, int q, int per_block) {
-    if (nb_total == 0) return 0;
-    const int kl = (nb_total - 1) / kQueueChunk;  // last chunk
-    const int nch = kl >= q ? (kl - q) / kXcds + 1 : 0;
-    const int nb = nch * kQueueChunk - (kl % kXcds == q ? (kl + 1) * kQueueChunk - nb_total : 0);
-    return nb * per_block;
+    constexpr int round = kXcds * kQueueChunk;
+    const int full = nb_total / round, rem = nb_total - full * round;
+    return (full * kQueueChunk + (rem > q ? (rem - q + kXcds - 1) / kXcds : 0)) * per_block;
 }
 // Schedule position of the qi-th block of queue q.
-__device__ __forceinline__ int queue_block(int q, int qi) {
-    return ((qi / kQueueChunk) * kXcds + q) * kQueueChunk + qi % kQueueChunk;
+__device__ __forceinline__ int queue_block(int nb_total, int q, int qi) {
+    constexpr int round = kXcds * kQueueChunk;
+    const int full = nb_total / round;
+    if (qi < full * kQueueChunk) return ((qi / kQueueChunk) * kXcds + q) * kQueueChunk + qi % kQueueChunk;
+    return full * round + (qi - full * kQueueChunk) * kXcds + q;
 }
 
 // LDS tiles of 64 bf16 per row ([rows][64]) store the 16-byte chunks of a

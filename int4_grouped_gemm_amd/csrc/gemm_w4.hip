@@ -22,7 +22,7 @@
 // The grid is persistent (as many workgroups as fit on the device) and
 // takes tiles from eight work queues, one per XCD. The schedule (the shared
 // expert's blocks, then the routed blocks in block_order, largest first,
-// read resolved from block_info) is dealt to the queues in turns of
+// read resolved from block_info) is dealt to the queues mostly in turns of
 // kQueueChunk consecutive blocks, so that most blocks of a hot expert meet
 // its weight slabs in one XCD's L2; a block's n-tiles are consecutive, so
 // that they meet the same A rows there too.
@@ -570,18 +570,17 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
     int toggle = 0;
 
     // Items of queue q: its blocks times the n-tiles times the K chunks (the
-    // chunks of a tile consecutive). Queue q owns the schedule's chunks of
-    // kQueueChunk blocks q, q + 8, ...; the last chunk may be short.
+    // chunks of a tile consecutive), dealt as queue_items describes.
     auto items_of = [&](int q) { return queue_items(nb_total, q, n_tiles * args.kc); };
     // Takes the next item of queue cq (one atomic) and resolves its rows,
     // expert and load plan (one load of block_info); it.valid = false if the
     // queue is empty.
     auto take = [&](Item<MI, W4>& it) {
         it.valid = false;
-        const int c = grab(args.sched + cq, s_slot, toggle);
+        const int c = grab(queue_ctr(args.sched, cq), s_slot, toggle);
         if (c >= items_of(cq)) return;
         const int ct = c / args.kc;  // tile of the queue
-        resolve_item<BM, GATED, W4>(args, queue_block(cq, ct / n_tiles), ct % n_tiles, c - ct * args.kc,
+        resolve_item<BM, GATED, W4>(args, queue_block(nb_total, cq, ct / n_tiles), ct % n_tiles, c - ct * args.kc,
                                     wave, lane, it);
     };
     // Every decision follows a value that grab() sent through LDS, so all
@@ -617,8 +616,8 @@ __global__ void __launch_bounds__(kGemmThreads, W4 ? Occ<BM>::WAVES_PER_SIMD : 2
     // A workgroup gets here once every queue has run out, so when the last
     // one arrives every item has been taken; it clears the counters for the
     // next launch.
-    if (tid == 0 && atomicAdd(args.sched + kXcds, 1) == (int)gridDim.x - 1) {
-        for (int i = 0; i <= kXcds; ++i) atomicExch(args.sched + i, 0);
+    if (tid == 0 && atomicAdd(queue_ctr(args.sched, kXcds), 1) == (int)gridDim.x - 1) {
+        for (int i = 0; i <= kXcds; ++i) atomicExch(queue_ctr(args.sched, i), 0);
     }
 }
 
@@ -650,11 +649,11 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD)
     int toggle = 0;
     auto take = [&](Item<MI, true>& it) {
         it.valid = false;
-        int c = grab(gu.sched + cq, s_slot, toggle);
+        int c = grab(queue_ctr(gu.sched, cq), s_slot, toggle);
         if (c < n_gu) {
-            resolve_item<BM, true, true>(gu, queue_block(cq, c / nt_gu), c % nt_gu, 0, wave, lane, it);
+            resolve_item<BM, true, true>(gu, queue_block(nb_total, cq, c / nt_gu), c % nt_gu, 0, wave, lane, it);
         } else if ((c -= n_gu) < n_dn) {
-            resolve_item<BM, false, true>(dn, queue_block(cq, c / nt_dn), c % nt_dn, 0, wave, lane, it);
+            resolve_item<BM, false, true>(dn, queue_block(nb_total, cq, c / nt_dn), c % nt_dn, 0, wave, lane, it);
         }
     };
     const uint32_t smem_addr = (uint32_t)(size_t)smem;
@@ -698,12 +697,12 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD)
 
     // The last workgroup to get here (every item taken and finished) clears
     // the queue counters and the block tallies for the next launch.
-    if (tid == 0) s_slot[2] = atomicAdd(gu.sched + kXcds, 1) == (int)gridDim.x - 1;
+    if (tid == 0) s_slot[2] = atomicAdd(queue_ctr(gu.sched, kXcds), 1) == (int)gridDim.x - 1;
     __syncthreads();
     if (s_slot[2]) {
         for (int i = tid; i < nb_total; i += kGemmThreads)
             __hip_atomic_store(gu.blk_done + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (tid <= kXcds) atomicExch(gu.sched + tid, 0);
+        if (tid <= kXcds) atomicExch(queue_ctr(gu.sched, tid), 0);
     }
 }
 
@@ -782,9 +781,9 @@ __global__ void __launch_bounds__(kGemmThreads, 4) moe_w4_gemm16(GemmArgs args) 
 
     auto take = [&](Item16& it) {
         it.valid = false;
-        const int c = grab(args.sched + cq, s_slot, toggle);
+        const int c = grab(queue_ctr(args.sched, cq), s_slot, toggle);
         if (c >= n_items) return;
-        const int vb = queue_block(cq, c / n_tiles), nt = c % n_tiles;
+        const int vb = queue_block(nb_total, cq, c / n_tiles), nt = c % n_tiles;
         int e = 0;
         bool shared;
         if (vb < args.shared_blocks) {
@@ -914,8 +913,8 @@ __global__ void __launch_bounds__(kGemmThreads, 4) moe_w4_gemm16(GemmArgs args) 
         }
         cur = nxt;
     }
-    if (tid == 0 && atomicAdd(args.sched + kXcds, 1) == (int)gridDim.x - 1) {
-        for (int i = 0; i <= kXcds; ++i) atomicExch(args.sched + i, 0);
+    if (tid == 0 && atomicAdd(queue_ctr(args.sched, kXcds), 1) == (int)gridDim.x - 1) {
+        for (int i = 0; i <= kXcds; ++i) atomicExch(queue_ctr(args.sched, i), 0);
     }
 }
 
@@ -1129,7 +1128,7 @@ static GemmArgs gate_up_args(const lily_moe_dims& d, const lily_moe_weights& w, 
     g.sw[1] = static_cast<const char*>(w.sh_up);
     g.N = d.F;
     g.K = d.H;
-    g.sched = r.sched;
+    g.sched = r.sched + kQueueBase;
     g.h_out = ws.h;
     g.kc = split_k(d, max_blocks, true);
     g.part = ws.part;
@@ -1145,7 +1144,7 @@ static GemmArgs down_args(const lily_moe_dims& d, const lily_moe_weights& w, con
     g.sw[0] = g.sw[1] = static_cast<const char*>(w.sh_down);
     g.N = d.H;
     g.K = d.F;
-    g.sched = r.sched + kQueueInts / 2;
+    g.sched = r.sched + kQueueBase + kQueueCtrs * kQueueLine;
     g.y_out = ws.y;
     g.kc = split_k(d, max_blocks, false);
     g.part = ws.part;
