@@ -187,6 +187,16 @@ def copy_calibration(dev):
     del src, dst
 
 
+def check_give_up(L, sched, what):
+    """Exit non-zero if a bounded device-wide wait gave up during the timed
+    steps (sched[30], which no call clears): the outputs, and so the timing,
+    are not valid (the workgroups were not all resident, or a device fault)."""
+    if int(sched[L.SCHED_GIVE_UP].item()) != 0:
+        print(f"{what}: a bounded device-wide wait gave up (sched[30] set): outputs and timing "
+              "are not valid", file=sys.stderr)
+        sys.exit(3)
+
+
 def main_prefill(args):
     import numpy as np
     import torch
@@ -263,6 +273,7 @@ def main_prefill(args):
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    check_give_up(L, routing.sched, "prefill")
 
     if args.copy_calibration:
         copy_calibration(dev)
@@ -472,10 +483,7 @@ def run_decode(args, n_layers_distinct, steps, warmup, path, brief=False):
     t1 = time.perf_counter()
     if getattr(args, "copy_calibration", False) and not brief:
         copy_calibration(dev)
-    if path != "layer" and int(routing.sched[30].item()) != 0:
-        print("decode: a device-wide barrier wait gave up (sched[30] set): the workgroups "
-              "were not all resident, outputs and timing are invalid", file=sys.stderr)
-        sys.exit(3)
+    check_give_up(L, routing.sched, "decode")
     ms_per_step = (t1 - t0) * 1e3 / steps
     us_per_layer = ms_per_step * 1e3 / n_layers
     # weight bytes a layer must read: the k routed experts and the shared one
@@ -617,6 +625,7 @@ def main_stack(args):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    check_give_up(L, routing.sched, "stack")
     s_step = (t1 - t0) / args.steps
     n_tok = cfg.T * cfg.chunks
     layer_flops = 2.0 * 3 * cfg.H * cfg.F * (cfg.k + 1) * n_tok * cfg.layers

@@ -135,6 +135,11 @@ typedef struct {
                               lily_moe_route clears the counters and leaves
                               the histograms zero, and every GEMM launch
                               leaves its counters zero when it completes.
+                              sched[30] is the give-up flag of the bounded
+                              device-wide waits (lily_moe_ffn's one launch,
+                              the decode kernels): set to 1 when one gave up
+                              (the outputs of that call are not valid), and
+                              sticky: no call clears it, the caller does.
                               Launches that share a routing buffer must be
                               ordered on one stream. */
 #define LILY_SCHED_INTS (1632 + 64 * 512 + 1)

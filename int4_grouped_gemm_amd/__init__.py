@@ -33,6 +33,7 @@ EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_by
            # include/lily_calib.h
            "lily_calib_mfma", "lily_calib_read")
 LILY_SCHED_INTS = 1632 + 64 * 512 + 1
+SCHED_GIVE_UP = 30  # sched[30]: sticky flag, set when a bounded device-wide wait gave up
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
 

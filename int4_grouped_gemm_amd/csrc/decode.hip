@@ -1206,7 +1206,7 @@ int launch_decode(const lily_moe_dims& d, const lily_moe_weights& w, const float
     static_assert(kQueueInts + kBarGroups * kBarLine <= kSchedInts, "barrier group counters");
     return launch_decode_with(d, w, logits, x, r.topk_ids, r.topk_w, out,
                               static_cast<uint16_t*>(workspace), r.sched + kDecodeBarrier,
-                              r.sched + kQueueInts, r.sched + kDecodeBarrier + 2, stream);
+                              r.sched + kQueueInts, r.sched + kGiveUpFlag, stream);
 }
 
 // Scratch of lily_moe_decode_noalloc, for callers that cannot allocate: the
@@ -1268,7 +1268,7 @@ int launch_decode_noalloc(const lily_moe_dims& d, const lily_moe_weights& w, con
                        status);
     if ((rc = check_launch("decode_noalloc clear"))) return rc;
     return launch_decode_with(d, w, logits, x, topk_ids, topk_w, out, h, ctr + kDecodeBarrier,
-                              ctr + kQueueInts, status ? status : ctr + kDecodeBarrier + 2, stream);
+                              ctr + kQueueInts, status ? status : ctr + kGiveUpFlag, stream);
 }
 
 int decode_stack_supported(const lily_moe_dims& d, int n_layers) {
@@ -1321,7 +1321,7 @@ int launch_decode_stack(const lily_moe_dims& d, int n_layers, const lily_moe_wei
     a.eps = eps;
     a.bar = sched + kDecodeBarrier;
     a.grp = sched + kQueueInts;
-    a.err = sched + kDecodeBarrier + 2;
+    a.err = sched + kGiveUpFlag;
     // One workgroup per compute unit (its LDS fills the compute unit): all
     // are resident at once, which the device-wide barrier and the exchanges
     // rely on.

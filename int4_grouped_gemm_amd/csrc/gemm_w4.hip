@@ -1256,7 +1256,7 @@ int launch_ffn(const lily_moe_dims& d, const lily_moe_weights& w, const uint16_t
     gu.shared_blocks = dn.shared_blocks = shared_blocks;
     gu.blk_done = dn.blk_done = r.sched + kQueueInts;
     gu.blk_need = dn.blk_need = d.F / GemmShape<true>::BN;
-    gu.sched_flag = dn.sched_flag = r.sched + kDecodeBarrier + 2;
+    gu.sched_flag = dn.sched_flag = r.sched + kGiveUpFlag;
     dn.sched = gu.sched;
     switch (d.tile_m) {
         case 32: return launch_ffn_bm<32>(gu, dn, max_blocks, stream);

@@ -272,8 +272,9 @@ __global__ void __launch_bounds__(kFinishThreads) route_finish_kernel(
             s_bst[E] = tot_blks;
         }
     }
-    if (lead)
-        for (int i = tid; i < kCounterInts; i += kFinishThreads) sched[i] = 0;
+    if (lead)  // the counters, but not the give-up flag, which stays until the caller clears it
+        for (int i = tid; i < kCounterInts; i += kFinishThreads)
+            if (i != kGiveUpFlag) sched[i] = 0;
     lds_sync();
 
     if (lead)

@@ -98,7 +98,9 @@ int launch_route_host(const lily_moe_dims& d, const float* logits, const lily_mo
         (rc = up(r.num_blocks, &nb, 1, "num_blocks")) ||
         (rc = up(r.block_order, order.data(), nb, "block_order")) ||
         (rc = up(r.block_info, info.data(), 4 * (size_t)nb, "block_info")) ||
-        (rc = hip_check(hipMemsetAsync(r.sched, 0, sizeof(int32_t) * kSchedInts, stream),
+        (rc = hip_check(hipMemsetAsync(r.sched, 0, sizeof(int32_t) * kGiveUpFlag, stream), "sched")) ||
+        (rc = hip_check(hipMemsetAsync(r.sched + kGiveUpFlag + 1, 0,
+                                       sizeof(int32_t) * (kSchedInts - kGiveUpFlag - 1), stream),
                         "sched")))
         return rc;
     // The host buffers must outlive the copies.

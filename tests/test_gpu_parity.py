@@ -106,7 +106,8 @@ def test_route_host_twin(case):
         lg = S.router_logits(S.CONFIGS[src], T=T)
     d = L.dims(T, 256, 128, E, k, M)
     r = L.alloc_routing(d)
-    r.sched.fill_(7)  # the twin must clear the GEMM counters itself
+    r.sched.fill_(7)  # the twin must clear the GEMM counters itself,
+    r.sched[L.SCHED_GIVE_UP] = 0  # but no call clears the give-up flag
     L.lily_moe_route_host(d, torch.from_numpy(lg).cuda(), r)
     torch.cuda.synchronize()
     G.compare_routing(G.routing_to_host(r), oracle.route(lg, k, M), M)
@@ -114,6 +115,23 @@ def test_route_host_twin(case):
     host = G.routing_to_host(r)
     for key in L.ROUTING_FIELDS:
         assert np.array_equal(gpu[key], host[key]), key
+
+
+@pytest.mark.parametrize("host", [False, True], ids=["gpu_route", "host_route"])
+def test_give_up_flag_sticky(host):
+    """sched[30], the give-up flag of the bounded device-wide waits, survives
+    both routes (which clear every counter around it) and the GEMMs: only the
+    caller clears it, so a give-up in any step of a run stays visible."""
+    _flush(f"give-up flag sticky, host route {host}")
+    d = L.dims(64, 256, 128, 16, 2, 32)
+    lg = np.random.default_rng(5).standard_normal((64, 16)).astype(np.float32)
+    r = L.alloc_routing(d)
+    r.sched[L.SCHED_GIVE_UP] = 1
+    (L.lily_moe_route_host if host else L.lily_moe_route)(d, torch.from_numpy(lg).cuda(), r)
+    torch.cuda.synchronize()
+    sched = r.sched.cpu().numpy()
+    assert sched[L.SCHED_GIVE_UP] == 1, "a route cleared the give-up flag"
+    assert not np.any(np.delete(sched, L.SCHED_GIVE_UP)), "counters left non-zero"
 
 
 def test_route_host_twin_forward():
