@@ -440,6 +440,45 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
             __hip_atomic_store(args.tile_ctr + lp.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
+    if constexpr (!GATED && NS == 3) {
+        // y through LDS, so that every store writes whole 128-byte lines: in
+        // the MFMA layout a 16-byte store covers 32 rows with 32 bytes each,
+        // and y's partial-line writes cost the launch ~5% (T = 2048) to 7%
+        // (T = 8192). Each wavefront turns its own 64 columns around in a
+        // private 4 KB of the third stage buffer (free: the next item's
+        // prefetch fills the first two, and its first step's barrier comes
+        // before that buffer is loaded again), 16 rows at a time: lanes of
+        // rows x write their 16-byte chunks, chunk index XOR-swizzled by the
+        // row against bank conflicts, then each lane reads one chunk of four
+        // rows and one store covers 4 rows x 256 bytes. A wavefront's LDS
+        // accesses run in order, so no barrier and no wait is needed between
+        // its writes and reads.
+        char* const tb = smem_p + Ld::A_OFF + 2 * Ld::A + (int)wave * 4096;
+        const int c = lane % 16, rq = lane / 16;
+        float* const ybase = args.y_out + lp.n0 + 64 * (int)wave + 4 * c;
+#pragma unroll
+        for (int i = 0; i < MIA; ++i)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                if (x / 16 == hf) {
+                    const int r = x % 16;
+#pragma unroll
+                    for (int g = 0; g < NI; ++g)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<f32x4*>(tb + r * 256 + ((8 * g + 2 * q + h) ^ r) * 16) =
+                                f32x4{acc[i][g][4 * q], acc[i][g][4 * q + 1], acc[i][g][4 * q + 2],
+                                      acc[i][g][4 * q + 3]};
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int rr = 4 * k + rq, row = 32 * i + 16 * hf + rr;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(tb + rr * 256 + (c ^ rr) * 16);
+                    if (row < rows) *reinterpret_cast<f32x4*>(ybase + (size_t)(r0 + row) * args.N) = v;
+                }
+            }
+        return;
+    }
     // Epilogue: 8 bytes of h (four bf16) or 16 bytes of y per store.
 #pragma unroll
     for (int i = 0; i < MIA; ++i) {
