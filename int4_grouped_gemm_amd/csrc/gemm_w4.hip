@@ -447,29 +447,45 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         // (T = 8192). Each wavefront turns its own 64 columns around in a
         // private 4 KB of the third stage buffer (free: the next item's
         // prefetch fills the first two, and its first step's barrier comes
-        // before that buffer is loaded again), 16 rows at a time: lanes of
-        // rows x write their 16-byte chunks, chunk index XOR-swizzled by the
-        // row against bank conflicts, then each lane reads one chunk of four
+        // before that buffer is loaded again), 16 rows at a time: the lanes
+        // write their 16-byte chunks (chunk index XOR-swizzled by the row
+        // against bank conflicts), then each lane reads one chunk of four
         // rows and one store covers 4 rows x 256 bytes. A wavefront's LDS
         // accesses run in order, so no barrier and no wait is needed between
         // its writes and reads.
         char* const tb = smem_p + Ld::A_OFF + 2 * Ld::A + (int)wave * 4096;
         const int c = lane % 16, rq = lane / 16;
+        const int y16 = lane % 16, q0 = (lane / 16) % 2;
         float* const ybase = args.y_out + lp.n0 + 64 * (int)wave + 4 * c;
 #pragma unroll
-        for (int i = 0; i < MIA; ++i)
+        for (int i = 0; i < MIA; ++i) {
+            // One v_permlane16_swap per register pairs column groups 2 q1 and
+            // 2 q1 + 1: then set 0 holds rows 0-15 of the sub-tile and set 1
+            // rows 16-31, lane l holding row l % 16 at column group 4 q1 +
+            // 2 q0 + h (q0 = l / 16 % 2), so that all 64 lanes write each band.
+            // (__float_as_uint, not __builtin_bit_cast: a bit_cast of a
+            // vector element compiles to a read of element 0 here.)
+            f32x4 band[2][NI][2];
+#pragma unroll
+            for (int g = 0; g < NI; ++g)
+#pragma unroll
+                for (int q1 = 0; q1 < 2; ++q1)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const auto sw = __builtin_amdgcn_permlane16_swap(
+                            __float_as_uint(acc[i][g][8 * q1 + e]), __float_as_uint(acc[i][g][8 * q1 + 4 + e]),
+                            false, false);
+                        band[0][g][q1][e] = __uint_as_float((uint32_t)sw[0]);
+                        band[1][g][q1][e] = __uint_as_float((uint32_t)sw[1]);
+                    }
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                if (x / 16 == hf) {
-                    const int r = x % 16;
 #pragma unroll
-                    for (int g = 0; g < NI; ++g)
+                for (int g = 0; g < NI; ++g)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<f32x4*>(tb + r * 256 + ((8 * g + 2 * q + h) ^ r) * 16) =
-                                f32x4{acc[i][g][4 * q], acc[i][g][4 * q + 1], acc[i][g][4 * q + 2],
-                                      acc[i][g][4 * q + 3]};
-                }
+                    for (int q1 = 0; q1 < 2; ++q1)
+                        *reinterpret_cast<f32x4*>(tb + y16 * 256 + ((8 * g + 4 * q1 + 2 * q0 + h) ^ y16) * 16) =
+                            band[hf][g][q1];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int rr = 4 * k + rq, row = 32 * i + 16 * hf + rr;
@@ -477,6 +493,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
                     if (row < rows) *reinterpret_cast<f32x4*>(ybase + (size_t)(r0 + row) * args.N) = v;
                 }
             }
+        }
         return;
     }
     // Epilogue: 8 bytes of h (four bf16) or 16 bytes of y per store.
