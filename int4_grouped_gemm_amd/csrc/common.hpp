@@ -32,6 +32,8 @@ static_assert(kPartBase + kMaxParts * kMaxExperts + 1 == kSchedInts, "sched layo
 // sched[28], sched[29]: the fused decode kernel's device-wide barrier
 // (arrivals, exits); sched[30]: set if one of its barrier waits gave up.
 constexpr int kDecodeBarrier = 28;
+constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor: raw, 32-bit data format
+constexpr int kCoherentLoad = 16;       // buffer load/store cache policy: sc1 (device-coherent)
 // sched[30], the give-up flag of every bounded device-wide wait (the decode
 // kernels' barriers and exchanges, the one-launch FFN's block tallies):
 // sticky, cleared by no launch, only by the caller.

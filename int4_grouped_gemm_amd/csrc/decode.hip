@@ -45,7 +45,6 @@ constexpr int kDecXChunks = 4;       // x 16-byte chunks staged per thread: T * 
 constexpr int kDecHChunks = kDecLdsWords / 4 / kDecThreads;  // h chunks staged per thread
 constexpr int kDecPiece = 8;         // output rows per phase B unit
 constexpr long kSpinTicks = 50000000;  // device-wide barrier wait limit: 0.5 s at 100 MHz
-constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor: raw, 32-bit data format
 
 struct DecodeArgs {
     const float* logits;  // [T, E]
@@ -579,7 +578,6 @@ __device__ __forceinline__ void store_tagged(uint64_t* p, uint64_t w) {
 // device-scope atomic loads are: the lane's offset in a VGPR, m's in an
 // SGPR, e's in the instruction. Bounded in time like the barrier wait: on a
 // timeout it flags the error and goes on.
-constexpr int kCoherentLoad = 16;  // buffer load cache policy: sc1
 template <int M, int EP>
 __device__ __forceinline__ void gather_tagged(const uint64_t* p, int n, uint32_t tag,
                                               uint64_t (&t)[M * EP], int w0, int wm,

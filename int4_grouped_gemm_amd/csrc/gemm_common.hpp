@@ -120,6 +120,16 @@ __device__ __forceinline__ void dma16_coh(const void* base, uint32_t lane_off, u
                  :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),
                     "s"(uniform_ptr(base)) : "memory");
 }
+// A 16-byte store through to the device-coherent level (sc1), as the
+// device-scope atomic stores are, at byte offset `off` of a buffer of
+// `bytes` bytes. A buffer-store builtin rather than inline asm: the compiler
+// then knows the store's data registers and keeps them intact until the
+// store has read them (it cannot see into an asm statement).
+__device__ __forceinline__ void store16_coherent(const void* base, uint32_t bytes, uint32_t off, u32x4 v) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(base)), 0, (int)bytes, kRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, kCoherentLoad);
+}
 __device__ __forceinline__ void dma4(const void* base, uint32_t lane_off, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                  :: "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(lane_off),

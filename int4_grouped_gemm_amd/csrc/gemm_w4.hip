@@ -496,31 +496,54 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
         }
         return;
     }
-    // Epilogue: 8 bytes of h (four bf16) or 16 bytes of y per store.
+    if constexpr (!GATED) {
+        // y of the shorter tiles (two stages: no free stage buffer to turn
+        // it around in): 16 bytes per store.
 #pragma unroll
-    for (int i = 0; i < MIA; ++i) {
-        const int row = 32 * i + x;
-        if (row >= rows) continue;
-        const size_t orow = (size_t)(r0 + row) * args.N;
+        for (int i = 0; i < MIA; ++i) {
+            const int row = 32 * i + x;
+            if (row >= rows) continue;
+            const size_t orow = (size_t)(r0 + row) * args.N;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (GATED) {
-                float v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = silu(acc[i][0][4 * q + j]) * acc[i][1][4 * q + j];
-                uint16_t* dst = args.h_out + orow + col0[0] + 8 * q + 4 * h;
-                const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-                if constexpr (FUSED)
-                    __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), (uint64_t)lo | ((uint64_t)hi << 32),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else
-                    *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
-            } else {
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int g = 0; g < NI; ++g)
                     *reinterpret_cast<f32x4*>(args.y_out + orow + col0[g] + 8 * q + 4 * h) =
                         f32x4{acc[i][g][4 * q], acc[i][g][4 * q + 1], acc[i][g][4 * q + 2],
                               acc[i][g][4 * q + 3]};
+        }
+        return;
+    }
+    // Epilogue: h, 16 bytes per store. In the MFMA layout lanes x and x + 32
+    // hold row x, four features each per column group q; one
+    // v_permlane32_swap per pair of registers gathers features 8 q .. 8 q + 7
+    // of groups q = 2 q1 (lane x) and 2 q1 + 1 (lane x + 32) in one lane
+    // each, so that a store writes 32 rows x 32 contiguous bytes instead of
+    // 32 rows x 16 bytes.
+    const uint32_t h_bytes = (uint32_t)((size_t)(args.P + args.T) * args.N * 2);
+#pragma unroll
+    for (int i = 0; i < MIA; ++i) {
+        const int row = 32 * i + x;
+        const uint32_t hoff = (uint32_t)(((size_t)(r0 + row) * args.N + col0[0] + 8 * h) * 2);
+        uint16_t* const hrow = args.h_out + (size_t)(r0 + row) * args.N + col0[0] + 8 * h;
+#pragma unroll
+        for (int q1 = 0; q1 < 2; ++q1) {
+            uint32_t w[2][2];  // [q - 2 q1][features 0-1, 2-3]
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int q = 2 * q1 + k;
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = silu(acc[i][0][4 * q + j]) * acc[i][1][4 * q + j];
+                w[k][0] = pack_bf16x2(v[0], v[1]);
+                w[k][1] = pack_bf16x2(v[2], v[3]);
+            }
+            const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+            const u32x4 out = {(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
+            if (row < rows) {
+                if constexpr (FUSED) store16_coherent(args.h_out, h_bytes, hoff + 32 * q1, out);
+                else *reinterpret_cast<u32x4*>(hrow + 16 * q1) = out;
             }
         }
     }
