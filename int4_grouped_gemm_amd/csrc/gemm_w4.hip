@@ -498,20 +498,35 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& args, char* smem_p,
     }
     if constexpr (!GATED) {
         // y of the shorter tiles (two stages: no free stage buffer to turn
-        // it around in): 16 bytes per store.
+        // it around in), in half lines: one v_permlane16_swap per register
+        // pairs column groups 2 q1 and 2 q1 + 1, after which the first set
+        // holds rows 0-15 of the sub-tile and the second rows 16-31, each row
+        // in four lanes (l / 16 = 2 h + q0) with 64 contiguous bytes.
+        const int y16 = lane % 16, q0 = (lane / 16) % 2;
 #pragma unroll
-        for (int i = 0; i < MIA; ++i) {
-            const int row = 32 * i + x;
-            if (row >= rows) continue;
-            const size_t orow = (size_t)(r0 + row) * args.N;
+        for (int i = 0; i < MIA; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int g = 0; g < NI; ++g)
 #pragma unroll
-                for (int g = 0; g < NI; ++g)
-                    *reinterpret_cast<f32x4*>(args.y_out + orow + col0[g] + 8 * q + 4 * h) =
-                        f32x4{acc[i][g][4 * q], acc[i][g][4 * q + 1], acc[i][g][4 * q + 2],
-                              acc[i][g][4 * q + 3]};
-        }
+                for (int q1 = 0; q1 < 2; ++q1) {
+                    f32x4 lo, hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // (__float_as_uint, not __builtin_bit_cast: a bit_cast of
+                        // a vector element compiles to a read of element 0 here)
+                        const auto sw = __builtin_amdgcn_permlane16_swap(
+                            __float_as_uint(acc[i][g][8 * q1 + e]), __float_as_uint(acc[i][g][8 * q1 + 4 + e]),
+                            false, false);
+                        lo[e] = __uint_as_float((uint32_t)sw[0]);
+                        hi[e] = __uint_as_float((uint32_t)sw[1]);
+                    }
+                    const int col = col0[g] + 16 * q1 + 8 * q0 + 4 * h;
+                    const int row_lo = 32 * i + y16, row_hi = row_lo + 16;
+                    if (row_lo < rows)
+                        *reinterpret_cast<f32x4*>(args.y_out + (size_t)(r0 + row_lo) * args.N + col) = lo;
+                    if (row_hi < rows)
+                        *reinterpret_cast<f32x4*>(args.y_out + (size_t)(r0 + row_hi) * args.N + col) = hi;
+                }
         return;
     }
     // Epilogue: h, 16 bytes per store. In the MFMA layout lanes x and x + 32
