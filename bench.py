@@ -62,8 +62,12 @@ def parse():
                     choices=[WORKLOAD, "prefill512", "prefill8192", "decode40", "stack40"],
                     help="prefill2048_zipf (the headline), decode40 (T=1, 40-layer steps) or "
                          "stack40 (40 distinct layers, T=8192 in chunks of 2048, residual glue)")
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 1000 for a prefill layer, 50 for decode40 "
+                         "and stack40)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 200 for a prefill layer, 10 for "
+                         "decode40 and stack40)")
     ap.add_argument("--layers", type=int, default=None,
                     help="distinct layer weight sets (prefill: cycled, default 8; decode: "
                          "default 40, the stack's own depth)")
@@ -97,7 +101,13 @@ def parse():
                     help="measure the achievable MFMA and HBM-read peaks and the clock; with "
                          "--write-peaks, record them in profiles/peaks.json")
     ap.add_argument("--write-peaks", action="store_true")
-    return ap.parse_args()
+    args = ap.parse_args()
+    layer_step = args.workload not in ("decode40", "stack40")
+    if args.steps is None:
+        args.steps = 1000 if layer_step else 50
+    if args.warmup is None:
+        args.warmup = 200 if layer_step else 10
+    return args
 
 
 def stage_work(cfg, P):
@@ -237,7 +247,9 @@ def main_prefill(args):
         ("route", "gate_up", "down", "combine") if args.separate_gemms else
         ("route", "ffn", "combine"))
 
-    def step(i, ev=None):
+    def step(i, ev=None, only=None):
+        """One layer step; ev: events recorded around every stage's call, or
+        (only = a stage index) around that call alone."""
         layer = i % n_sets
         w = weights[layer]
         calls = []
@@ -257,20 +269,41 @@ def main_prefill(args):
             calls += [lambda: L.lily_moe_ffn(d, w, x, routing, ws, stream),
                       lambda: L.lily_moe_combine(d, routing, ws, out, stream)]
         for j, call in enumerate(calls):
-            if ev is not None:
+            if ev is not None and only is None:
                 ev[j].record(stream)
+            elif ev is not None and j == only:
+                ev[0].record(stream)
             call()
-        if ev is not None:
+            if ev is not None and j == only:
+                ev[1].record(stream)
+        if ev is not None and only is None:
             ev[len(calls)].record(stream)
 
+    # Untimed warmup (the clocks and the weight sets' first touches settle
+    # over the first hundred steps or so), then one untimed pass with events
+    # around every stage for the stage breakdown and the dominant stage.
     for i in range(args.warmup):
         step(i)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-              for _ in range(args.steps)]
+    n_split = 50
+    split_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+                for _ in range(n_split)]
+    for i in range(n_split):
+        step(args.warmup + i, split_ev[i])
+    torch.cuda.synchronize()
+    stage_ms = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in split_ev]))
+                for j, s in enumerate(stages)}
+    dom = max(stages, key=lambda s: stage_ms[s])
+    dom_j = stages.index(dom)
+
+    # The timed steps: events only around the dominant stage's launch, on
+    # the stream it runs on, for its roofline.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(2):  # the first steps after the event pass
+        step(args.warmup + n_split + i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(args.warmup + n_split + 2 + i, events[i], dom_j)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     check_give_up(L, routing.sched, "prefill")
@@ -280,17 +313,15 @@ def main_prefill(args):
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = cfg.T / ((t1 - t0) / args.steps)
-    stage_ms = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
-                for j, s in enumerate(stages)}
+    dom_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events]))
 
     work = stage_work(cfg, P)
-    dom = max(stages, key=lambda s: stage_ms[s])
     bound, amount = work[dom]
     if bound == "mfma":
-        achieved = amount / (stage_ms[dom] * 1e-3) / 1e12
+        achieved = amount / (dom_ms * 1e-3) / 1e12
         peak, unit = PEAK_MFMA_BF16_TFLOPS, "TFLOP/s"
     else:
-        achieved = amount / (stage_ms[dom] * 1e-3) / 1e9
+        achieved = amount / (dom_ms * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -301,6 +332,7 @@ def main_prefill(args):
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                "kernel_ms": round(dom_ms, 4),
                 "frac_of_measured": frac_of_measured(bound, achieved)}
 
     # whole-layer fractions: useful flops and the weight bytes one layer must read
@@ -352,21 +384,28 @@ def main_prefill(args):
     torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
+        # The oracle on the same steps: route + forward of the layer weight
+        # sets in the GPU's order, until about ten seconds of CPU work (the
+        # inputs' generation is not timed).
         import oracle
-        lw = S.layer_weights(cfg, 0)
-        lg = S.router_logits(cfg, 0)
         xs = S.activations(cfg)
         ntok = min(args.cpu_tokens, cfg.T)
-        c0 = time.perf_counter()
-        rr = oracle.route(lg, cfg.k, args.tile_m)
-        oracle.forward(xs, rr["topk_ids"], rr["topk_w"], oracle.getter_from_layer(lw),
-                       cfg.H, cfg.F, cfg.E, tokens=list(range(ntok)))
-        c1 = time.perf_counter()
+        cpu_s, layers_done = 0.0, 0
+        while layers_done < n_sets and cpu_s < 10.0:
+            lw = S.layer_weights(cfg, layers_done)
+            lg = S.router_logits(cfg, layers_done)
+            c0 = time.perf_counter()
+            rr = oracle.route(lg, cfg.k, args.tile_m)
+            oracle.forward(xs, rr["topk_ids"], rr["topk_w"], oracle.getter_from_layer(lw),
+                           cfg.H, cfg.F, cfg.E, tokens=list(range(ntok)))
+            cpu_s += time.perf_counter() - c0
+            layers_done += 1
         result["cpu_baseline"] = {
-            "value": round(ntok / (c1 - c0), 2), "unit": "tokens/s",
+            "value": round(ntok * layers_done / cpu_s, 2), "unit": "tokens/s",
             "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"route of all {cfg.T} tokens + forward of {ntok} tokens of layer 0 "
-                      f"(dequant of the experts they use included), {c1 - c0:.1f} s",
+            "sample": f"{layers_done} layer steps (weight sets 0..{layers_done - 1}), each the "
+                      f"route of all {cfg.T} tokens + forward of {ntok} tokens (dequant of the "
+                      f"experts they use included), {cpu_s:.1f} s",
         }
 
     if args.workload == WORKLOAD and not (args.no_extra or args.router or args.route_host
