@@ -12,10 +12,12 @@ import dataclasses
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblily_moe.so")
+TRACE_LIB_PATH = os.path.join(HERE, "liblily_moe_trace.so")  # the same, with the FFN item trace
 
 LILY_OK = 0
 LILY_ERR_INVALID_ARG = -1
@@ -31,7 +33,9 @@ EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_by
            "lily_residual_norm",
            "lily_last_error",
            # include/lily_calib.h
-           "lily_calib_mfma", "lily_calib_read")
+           "lily_calib_mfma", "lily_calib_read",
+           # include/lily_trace.h
+           "lily_trace_ffn_items")
 LILY_SCHED_INTS = 1632 + 64 * 512 + 1
 SCHED_GIVE_UP = 30  # sched[30]: sticky flag, set when a bounded device-wide wait gave up
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
@@ -150,6 +154,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_calib_read.restype = ctypes.c_int
     lib.lily_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_trace_ffn_items.restype = ctypes.c_int
+    lib.lily_trace_ffn_items.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -422,6 +428,27 @@ def lily_calib_read(src, nbytes: int, grid: int, dma: bool, sink, stream=None) -
     lib = load()
     _check(lib.lily_calib_read(_ptr(src), nbytes, grid, 1 if dma else 0, _ptr(sink),
                                _stream(stream)), lib)
+
+
+def load_trace() -> ctypes.CDLL:
+    """Make the tracing build (liblily_moe_trace.so) the library that every
+    call of this module goes through; call it before any other call."""
+    global _lib
+    _lib = load(TRACE_LIB_PATH)
+    return _lib
+
+
+TRACE_SLOTS = 32  # item rows per workgroup in the FFN trace; row 32 is the launch row
+
+
+def lily_trace_ffn_items(max_wgs: int = 1024, stream=None) -> np.ndarray:
+    """The item trace of the last lily_moe_ffn launch (tracing build only):
+    uint64 [n][33][4], as lily_trace.h describes."""
+    lib = load()
+    buf = np.zeros((max_wgs, TRACE_SLOTS + 1, 4), dtype=np.uint64)
+    n = lib.lily_trace_ffn_items(buf.ctypes.data_as(ctypes.c_void_p), max_wgs, _stream(stream))
+    _check(min(n, 0), lib)
+    return buf[:n]
 
 
 # ----------------------------------------------------------------- allocation

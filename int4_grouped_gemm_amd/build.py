@@ -1,4 +1,6 @@
-"""Build ``liblily_moe.so`` (HIP, gfx950) in-tree with hipcc.
+"""Build ``liblily_moe.so`` (HIP, gfx950) in-tree with hipcc, and its
+tracing twin ``liblily_moe_trace.so`` (the same objects but gemm_w4.hip,
+compiled with LILY_TRACE_ITEMS: the item trace of lily_trace.h).
 
 Every source is compiled for gfx950 only. Packed FP32 instructions are
 disabled on the device side (``-packed-fp32-ops``); the host pass warns that
@@ -17,6 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblily_moe.so")
+TRACE_LIB = os.path.join(HERE, "liblily_moe_trace.so")
 
 SOURCES = ["abi.hip", "route.hip", "route_host.hip", "gemm_w4.hip", "decode.hip", "router.hip",
            "residual.hip", "calib.hip"]
@@ -33,26 +36,35 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, trace: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_trace.o" if trace else ".o"))
+    cmd = [_hipcc(), *FLAGS, *(["-DLILY_TRACE_ITEMS"] if trace else []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every HIP source for gfx950 and link the shared library."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile every HIP source for gfx950 and link the shared library and its
+    tracing twin."""
+    os.makedirs(BUILD, exist_ok=True)
+    units = [(src, False) for src in SOURCES] + [("gemm_w4.hip", True)]
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(units))) as ex:
+        objs = list(ex.map(lambda u: _compile(*u), units))
+    _link(objs[:len(SOURCES)], LIB)
+    traced = [objs[-1] if src == "gemm_w4.hip" else o for src, o in zip(SOURCES, objs)]
+    _link(traced, TRACE_LIB)
     return LIB
 
 

@@ -3,6 +3,7 @@
 #include <stdio.h>
 
 #include "common.hpp"
+#include "lily_trace.h"
 
 namespace lily {
 
@@ -440,6 +441,10 @@ int lily_moe_decode_stack(const lily_moe_dims* dims, int32_t n_layers,
     if ((rc = check_workspace(*dims, workspace, workspace_bytes))) return rc;
     return launch_decode_stack(*dims, n_layers, layers, logits, x0, r, outs, topk_ids, topk_w,
                                sched, eps, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int lily_trace_ffn_items(unsigned long long* dst, int32_t max_wgs, void* stream) {
+    return trace_ffn_items(dst, max_wgs, reinterpret_cast<hipStream_t>(stream));
 }
 
 const char* lily_last_error(void) { return g_last_error; }

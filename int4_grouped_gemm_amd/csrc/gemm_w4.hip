@@ -34,6 +34,18 @@
 
 namespace lily {
 
+#ifdef LILY_TRACE_ITEMS
+// Item trace of moe_w4_ffn, compiled into the tracing build of the library
+// only (liblily_moe_trace.so). Per workgroup and item, in the order taken:
+// the wall clock (s_memrealtime, 100 MHz) at its start and at its end (after
+// its stores), what it was, and the ticks it waited for its block's gate/up
+// tiles; slot kTraceSlots: the launch entry and exit, the items run and the
+// grid size. Thread 0 of each workgroup writes its own rows.
+constexpr int kTraceWgs = 1024, kTraceSlots = 32;
+__device__ unsigned long long g_ffn_trace[kTraceWgs][kTraceSlots + 1][4];
+__device__ unsigned long long g_ffn_wait[kTraceWgs];
+#endif
+
 // Tile geometry. A workgroup has 4 wavefronts that split the output columns;
 // every wavefront covers all BM rows of the block. The workgroup owns 256
 // weight rows, two packed slabs: for the gate/up GEMM slab n-tile of the
@@ -169,6 +181,10 @@ __device__ __forceinline__ void wait_block_done(const GemmArgs& args, int vb) {
             break;
         }
     }
+#ifdef LILY_TRACE_ITEMS
+    if (threadIdx.x == 0 && blockIdx.x < kTraceWgs)
+        g_ffn_wait[blockIdx.x] += __builtin_amdgcn_s_memrealtime() - t0;
+#endif
 }
 
 // Loads, multiplies and stores one tile. `prep_next` runs between the
@@ -751,9 +767,25 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD)
         }
     };
     const uint32_t smem_addr = (uint32_t)(size_t)smem;
+#ifdef LILY_TRACE_ITEMS
+    const unsigned long long t_entry = __builtin_amdgcn_s_memrealtime();
+    const bool traced = tid == 0 && blockIdx.x < kTraceWgs;
+    unsigned long long(*trace)[4] = g_ffn_trace[blockIdx.x < kTraceWgs ? blockIdx.x : 0];
+    int n_run = 0;
+    if (traced) g_ffn_wait[blockIdx.x] = 0;
+#endif
     Item<MI, true> cur;
     take(cur);
     while (cur.valid) {
+#ifdef LILY_TRACE_ITEMS
+        if (traced && n_run < kTraceSlots) {
+            trace[n_run][0] = __builtin_amdgcn_s_memrealtime();
+            trace[n_run][2] = (unsigned long long)cur.mia | ((unsigned long long)cur.down << 8) |
+                              ((unsigned long long)cur.n0 << 16) |
+                              ((unsigned long long)cur.vb << 32);
+            trace[n_run][3] = g_ffn_wait[blockIdx.x];
+        }
+#endif
         Item<MI, true> nxt;
         // As in the separate launches; a down item's first stages are
         // prefetched only if its block is already complete.
@@ -786,8 +818,23 @@ __global__ void __launch_bounds__(kGemmThreads, Occ<BM>::WAVES_PER_SIMD)
                 gemm_main<BM, false, (MI > 2 ? 2 : 1), true, true>(dn, smem, cur, wave, s_slot + 2, prep);
             else gemm_main<BM, false, (MI > 3 ? 3 : 1), true, true>(dn, smem, cur, wave, s_slot + 2, prep);
         }
+#ifdef LILY_TRACE_ITEMS
+        if (traced && n_run < kTraceSlots) {
+            trace[n_run][1] = __builtin_amdgcn_s_memrealtime();
+            trace[n_run][3] = g_ffn_wait[blockIdx.x] - trace[n_run][3];
+        }
+        ++n_run;
+#endif
         cur = nxt;
     }
+#ifdef LILY_TRACE_ITEMS
+    if (traced) {
+        trace[kTraceSlots][0] = t_entry;
+        trace[kTraceSlots][1] = __builtin_amdgcn_s_memrealtime();
+        trace[kTraceSlots][2] = (unsigned long long)n_run;
+        trace[kTraceSlots][3] = gridDim.x;
+    }
+#endif
 
     // The last workgroup to get here (every item taken and finished) clears
     // the queue counters and the block tallies for the next launch.
@@ -1381,5 +1428,27 @@ int launch_combine(const lily_moe_dims& d, const ForwardWorkspace& ws, const lil
     return check_launch("combine");
 }
 
+
+// Copies the item trace of the last moe_w4_ffn launch (tracing build only).
+int trace_ffn_items(unsigned long long* dst, int max_wgs, hipStream_t stream) {
+#ifdef LILY_TRACE_ITEMS
+    if (!dst || max_wgs < 1)
+        return set_error(LILY_ERR_INVALID_ARG, "trace_ffn_items: dst non-NULL, max_wgs >= 1");
+    const int n = max_wgs < kTraceWgs ? max_wgs : kTraceWgs;
+    const size_t row = sizeof(g_ffn_trace[0]);
+    if (hipStreamSynchronize(stream) != hipSuccess ||
+        hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_ffn_trace), row * n, 0, hipMemcpyDeviceToHost) !=
+            hipSuccess)
+        return set_error(LILY_ERR_HIP, "trace_ffn_items: copy failed");
+    return n;
+#else
+    (void)dst;
+    (void)max_wgs;
+    (void)stream;
+    return set_error(LILY_ERR_UNSUPPORTED,
+                     "trace_ffn_items: this library was built without the item trace "
+                     "(liblily_moe_trace.so has it)");
+#endif
+}
 
 }  // namespace lily

@@ -10,7 +10,7 @@ import pytest
 import int4_grouped_gemm_amd as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("lily_moe.h", "lily_calib.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("lily_moe.h", "lily_calib.h", "lily_trace.h")]
 
 
 @pytest.fixture(scope="module")
@@ -277,3 +277,20 @@ def test_decode_rejects(lib):
     rc = lib.lily_moe_decode(ctypes.byref(d), ctypes.byref(weights()), FAKE, FAKE,
                              ctypes.byref(routing()), FAKE, FAKE, need - 1, None)
     assert rc == L.LILY_ERR_WORKSPACE
+
+
+def test_trace_only_in_the_tracing_build(lib):
+    """The item trace is the tracing build's: the ordinary library reports it
+    as unsupported, the tracing build exports the same symbols and rejects a
+    NULL destination before any device call."""
+    buf = (ctypes.c_ulonglong * 4)()
+    assert lib.lily_trace_ffn_items(buf, 1, None) == L.LILY_ERR_UNSUPPORTED
+    assert "built without" in lib.lily_last_error().decode()
+    if not os.path.exists(L.TRACE_LIB_PATH):
+        from int4_grouped_gemm_amd import build
+        build.build()
+    tl = L.load(L.TRACE_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(tl, n), f"{n} not exported by the tracing build"
+    assert tl.lily_trace_ffn_items(None, 1, None) == L.LILY_ERR_INVALID_ARG
+    assert tl.lily_trace_ffn_items(buf, 0, None) == L.LILY_ERR_INVALID_ARG

@@ -340,6 +340,52 @@ def test_ffn_one_launch(name, tile_m):
         assert not np.any(r.sched.cpu().numpy()), "counters, tallies and the give-up flag stay zero"
 
 
+@pytest.mark.parametrize("name,tile_m", [("prefill512", 128), ("tiny", 32)])
+def test_ffn_item_trace(name, tile_m):
+    """The tracing build (liblily_moe_trace.so) writes the same h and y as
+    the library, bit for bit, and its item trace accounts for every work
+    item of the launch exactly once: each block's gate/up and down n-tiles,
+    with start <= end and waits on down items only."""
+    cfg = S.CONFIGS[name]
+    _flush(f"ffn item trace {name} tile_m={tile_m}")
+    d = L.dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, tile_m)
+    w = L.weights_from_host(S.layer_weights(cfg, 0))
+    xd = G.to_dev_bits(S.activations(cfg))
+    r = G.route_gpu(d, S.router_logits(cfg))
+    ws = L.alloc_workspace(d)
+    h, y = L.workspace_views(d, ws)
+    L.lily_moe_ffn(d, w, xd, r, ws)
+    torch.cuda.synchronize()
+    want_h, want_y = h.clone(), y.clone()
+    h.fill_(0)
+    y.fill_(0)
+    prod = L.load()
+    try:
+        L.load_trace()
+        L.lily_moe_ffn(d, w, xd, r, ws)
+        tr = L.lily_trace_ffn_items()
+    finally:
+        L._lib = prod
+    assert torch.equal(h, want_h) and torch.equal(y, want_y), "the tracing build's h or y differs"
+    assert not np.any(r.sched.cpu().numpy()), "counters, tallies and the give-up flag stay zero"
+    grid = int(tr[0, -1, 3])
+    assert 1 <= grid <= tr.shape[0]
+    n_blocks = int(r.num_blocks.cpu()[0]) + (cfg.T + tile_m - 1) // tile_m
+    nt_gu, nt_dn = cfg.F // 128, cfg.H // 256
+    seen = []
+    for wg in range(grid):
+        n = int(tr[wg, -1, 2])
+        assert n <= L.TRACE_SLOTS, "more items than the trace records"
+        assert tr[wg, -1, 0] <= tr[wg, -1, 1]
+        for st, en, info, wait in tr[wg, :n].astype(np.int64):
+            down = int((info >> 8) & 1)
+            assert st <= en and (down or wait == 0)
+            seen.append((down, int(info >> 32), int((info >> 16) & 0xFFFF)))
+    want = sorted([(0, b, 128 * t) for b in range(n_blocks) for t in range(nt_gu)] +
+                  [(1, b, 256 * t) for b in range(n_blocks) for t in range(nt_dn)])
+    assert sorted(seen) == want, "the trace does not hold every item exactly once"
+
+
 # ------------------------------------------------------------------- split K
 
 @pytest.mark.parametrize("T,tile_m", [(1, 32), (1, 128), (4, 32), (8, 64), (3, 128)])
