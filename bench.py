@@ -12,10 +12,13 @@ resident in HBM before timing starts.
 
 Prints ONE JSON line. ``value`` is MoE-layer tokens/s = T / (seconds per
 step), timed with the wall clock between two device synchronisations.
-``roofline`` reports the dominant kernel: its algorithmic flops (or bytes)
-per launch over its average duration from HIP events recorded on the launch
-stream around every launch in the timed region. ``cpu_baseline`` times the
-CPU oracle on a bounded sample of the same workload.
+A prefill run does 200 untimed warm-up steps (the clocks settle over the
+first hundred or so), 50 untimed steps with HIP events around every stage
+(``stages_ms``, and the choice of the dominant stage), then the 1000 timed
+steps. ``roofline`` reports the dominant kernel: its algorithmic flops (or
+bytes) per launch over its average duration from the HIP events recorded on
+the launch stream around its launch in every timed step. ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload (about 10 s).
 
 By default the run also measures the other configurations of the layer at
 their stated sizes and reports them as extra keys (``extra``): one layer at
