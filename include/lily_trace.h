@@ -1,14 +1,17 @@
 /*
- * lily_trace.h: the item trace of the one-launch expert FFN (gfx950).
+ * lily_trace.h: timelines of the one-launch expert FFN and of the
+ * whole-step decode kernel (gfx950).
  *
  * The tracing build of the library (liblily_moe_trace.so: the same sources,
- * with moe_w4_ffn compiled with LILY_TRACE_ITEMS) records, for every
- * workgroup of each lily_moe_ffn launch (lily_moe_forward's default path),
- * when each of its work items started and ended and how long it waited for
- * its block's gate/up tiles, so that the launch's timeline (occupancy, the
- * end-of-launch tail, per-queue balance) can be read back. Its outputs are
- * the product library's, bit for bit; the ordinary library
- * (liblily_moe.so) exports the same call and returns LILY_ERR_UNSUPPORTED.
+ * with gemm_w4.hip and decode.hip compiled with LILY_TRACE_ITEMS) records,
+ * for every workgroup of each lily_moe_ffn launch (lily_moe_forward's
+ * default path), when each of its work items started and ended and how long
+ * it waited for its block's gate/up tiles, so that the launch's timeline
+ * (occupancy, the end-of-launch tail, per-queue balance) can be read back;
+ * and, for every workgroup and layer of each lily_moe_decode_stack launch,
+ * when it passed the points between the layer's phases. Its outputs are the
+ * product library's, bit for bit; the ordinary library (liblily_moe.so)
+ * exports the same calls and returns LILY_ERR_UNSUPPORTED.
  *
  * Conventions as in lily_moe.h: 0 or a positive count on success, a
  * negative LILY_ERR_* code with lily_last_error() describing it.
@@ -35,6 +38,21 @@ extern "C" {
    dst, max_wgs < 1), LILY_ERR_UNSUPPORTED (not the tracing build),
    LILY_ERR_HIP. */
 int lily_trace_ffn_items(unsigned long long* dst, int32_t max_wgs, void* stream);
+
+/* Waits for `stream`, then copies the phase trace of the last
+   lily_moe_decode_stack launch on the current device into dst (host memory,
+   caller-owned): uint64 [n][64][8], n = min(max_wgs, 256) workgroups, layers
+   0..63, ticks of the 100 MHz wall clock. Points per (workgroup, layer):
+   0 layer start, 1 previous layer's output gathered and added to r, 2 x of
+   the layer staged (norm done), 3 the workgroup's phase A part sums ready,
+   4 its h words stored, 5 all h gathered by its compute wavefronts (points
+   0-5 by the lead wavefront); 6 h gathered by compute wavefront 0, 7 the
+   workgroup's phase B sums ready (compute wavefront 0; only workgroups with a
+   phase B unit write it). Rows of layers past the launch's, and of
+   workgroups past its grid, hold stale values. Returns n. Errors:
+   LILY_ERR_INVALID_ARG, LILY_ERR_UNSUPPORTED (not the tracing build),
+   LILY_ERR_HIP. */
+int lily_trace_decode_stack(unsigned long long* dst, int32_t max_wgs, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_by
            # include/lily_calib.h
            "lily_calib_mfma", "lily_calib_read",
            # include/lily_trace.h
-           "lily_trace_ffn_items")
+           "lily_trace_ffn_items", "lily_trace_decode_stack")
 LILY_SCHED_INTS = 1632 + 64 * 512 + 1
 SCHED_GIVE_UP = 30  # sched[30]: sticky flag, set when a bounded device-wide wait gave up
 WEIGHT_FIELDS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
@@ -156,6 +156,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.lily_trace_ffn_items.restype = ctypes.c_int
     lib.lily_trace_ffn_items.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.lily_trace_decode_stack.restype = ctypes.c_int
+    lib.lily_trace_decode_stack.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -447,6 +449,16 @@ def lily_trace_ffn_items(max_wgs: int = 1024, stream=None) -> np.ndarray:
     lib = load()
     buf = np.zeros((max_wgs, TRACE_SLOTS + 1, 4), dtype=np.uint64)
     n = lib.lily_trace_ffn_items(buf.ctypes.data_as(ctypes.c_void_p), max_wgs, _stream(stream))
+    _check(min(n, 0), lib)
+    return buf[:n]
+
+
+def lily_trace_decode_stack(max_wgs: int = 256, stream=None) -> np.ndarray:
+    """The phase trace of the last lily_moe_decode_stack launch (tracing build
+    only): uint64 [n][64][8], as lily_trace.h describes."""
+    lib = load()
+    buf = np.zeros((max_wgs, 64, 8), dtype=np.uint64)
+    n = lib.lily_trace_decode_stack(buf.ctypes.data_as(ctypes.c_void_p), max_wgs, _stream(stream))
     _check(min(n, 0), lib)
     return buf[:n]
 

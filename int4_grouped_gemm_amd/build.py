@@ -1,6 +1,6 @@
 """Build ``liblily_moe.so`` (HIP, gfx950) in-tree with hipcc, and its
-tracing twin ``liblily_moe_trace.so`` (the same objects but gemm_w4.hip,
-compiled with LILY_TRACE_ITEMS: the item trace of lily_trace.h).
+tracing twin ``liblily_moe_trace.so`` (the same objects but gemm_w4.hip and
+decode.hip, compiled with LILY_TRACE_ITEMS: the traces of lily_trace.h).
 
 Every source is compiled for gfx950 only. Packed FP32 instructions are
 disabled on the device side (``-packed-fp32-ops``); the host pass warns that
@@ -59,12 +59,13 @@ def build(jobs: int = 8) -> str:
     """Compile every HIP source for gfx950 and link the shared library and its
     tracing twin."""
     os.makedirs(BUILD, exist_ok=True)
-    units = [(src, False) for src in SOURCES] + [("gemm_w4.hip", True)]
+    traced_src = ("gemm_w4.hip", "decode.hip")
+    units = [(src, False) for src in SOURCES] + [(src, True) for src in traced_src]
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(units))) as ex:
         objs = list(ex.map(lambda u: _compile(*u), units))
     _link(objs[:len(SOURCES)], LIB)
-    traced = [objs[-1] if src == "gemm_w4.hip" else o for src, o in zip(SOURCES, objs)]
-    _link(traced, TRACE_LIB)
+    tobj = dict(zip(traced_src, objs[len(SOURCES):]))
+    _link([tobj.get(src, o) for src, o in zip(SOURCES, objs)], TRACE_LIB)
     return LIB
 
 

@@ -447,6 +447,10 @@ int lily_trace_ffn_items(unsigned long long* dst, int32_t max_wgs, void* stream)
     return trace_ffn_items(dst, max_wgs, reinterpret_cast<hipStream_t>(stream));
 }
 
+int lily_trace_decode_stack(unsigned long long* dst, int32_t max_wgs, void* stream) {
+    return trace_decode_stack(dst, max_wgs, reinterpret_cast<hipStream_t>(stream));
+}
+
 const char* lily_last_error(void) { return g_last_error; }
 
 }  // extern "C"

@@ -84,6 +84,7 @@ struct LaunchError {
 size_t decode_workspace_bytes(const lily_moe_dims& d);  // 0 when T is too large
 
 int trace_ffn_items(unsigned long long* dst, int max_wgs, hipStream_t stream);
+int trace_decode_stack(unsigned long long* dst, int max_wgs, hipStream_t stream);
 
 // Records the thread's last error text; returns code.
 int set_error(int code, const char* fmt, ...);

@@ -665,6 +665,28 @@ __device__ __forceinline__ int loads_of(int dw, int lo, int hi) {
     return upto(hi) - upto(lo);
 }
 
+#ifdef LILY_TRACE_ITEMS
+// Phase trace of moe_decode_stack_kernel, compiled into the tracing build of
+// the library only (liblily_moe_trace.so): per workgroup and layer, the wall
+// clock (s_memrealtime, 100 MHz) at eight points, written by lane 0 of the
+// wavefront that reaches them. Lead wavefront: 0 layer start, 1 previous
+// output gathered and added to r, 2 x staged (norm done), 3 phase A part sums
+// of the workgroup ready, 4 h words stored, 5 h gathered by the compute
+// wavefronts. Compute wavefront 0: 6 its h gathered, 7 phase B sums of the
+// workgroup ready (only in workgroups with a phase B unit).
+constexpr int kTraceStackWgs = 256, kTraceStackLayers = 64;
+__device__ unsigned long long g_stack_trace[kTraceStackWgs][kTraceStackLayers][8];
+#define STACK_TRACE(l, i)                                                                       \
+    do {                                                                                        \
+        if (lane == 0 && blockIdx.x < kTraceStackWgs && (l) < kTraceStackLayers)                \
+            g_stack_trace[blockIdx.x][(l)][(i)] = __builtin_amdgcn_s_memrealtime();             \
+    } while (0)
+#else
+#define STACK_TRACE(l, i) \
+    do {                  \
+    } while (0)
+#endif
+
 __global__ void __launch_bounds__(kStkThreads) moe_decode_stack_kernel(StackArgs a) {
     // Gate/up buffer of a layer: per unit (slot s), the gate then the up
     // weights: q as [quad i][lane][16 bytes] (the lane's slice of quad i),
@@ -902,6 +924,7 @@ __global__ void __launch_bounds__(kStkThreads) moe_decode_stack_kernel(StackArgs
                     }
                 }
             }
+            if (wv == 0) STACK_TRACE(l, 6);
             lds_barrier();  // h staged; layer l's down share landed
             if (has_b) {
                 // Phase B: rounds rho = w + 8 n of the workgroup's unit, like
@@ -929,6 +952,7 @@ __global__ void __launch_bounds__(kStkThreads) moe_decode_stack_kernel(StackArgs
             // complete in order.
             if (wv == 0 && has_b) {
                 wait_count(&s_done_b, kDecWaves * (l + 1));
+                STACK_TRACE(l, 7);
                 float o = 0.0f;
                 if (lane < kDecPiece)
 #pragma unroll
@@ -995,6 +1019,7 @@ __global__ void __launch_bounds__(kStkThreads) moe_decode_stack_kernel(StackArgs
         }
         for (int l = 0; l < L; ++l) {
             const uint32_t tag = (uint32_t)l + 1;
+            STACK_TRACE(l, 0);
             if (l > 0) {
                 // out_{l-1} (tag l), elements 4 l + 256 m .. + 3 as two pairs;
                 // r_l = r_{l-1} + out_{l-1}.
@@ -1013,6 +1038,7 @@ __global__ void __launch_bounds__(kStkThreads) moe_decode_stack_kernel(StackArgs
                         *reinterpret_cast<f32x4*>(s_r + 4 * lane + 256 * m) = f;
                     }
             }
+            STACK_TRACE(l, 1);
             float rv[kStkRSlots][4];
 #pragma unroll
             for (int m = 0; m < kStkRSlots; ++m)
@@ -1063,7 +1089,9 @@ __global__ void __launch_bounds__(kStkThreads) moe_decode_stack_kernel(StackArgs
                 }
             }
             lds_barrier();  // x ready
+            STACK_TRACE(l, 2);
             wait_count(&s_done_a, kDecWaves * (l + 1));  // part sums of phase A ready
+            STACK_TRACE(l, 3);
             if (l == 0) {   // every workgroup's tag clears have landed
                 if (lane == 0) {
                     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -1104,7 +1132,9 @@ __global__ void __launch_bounds__(kStkThreads) moe_decode_stack_kernel(StackArgs
             asm volatile("" ::: "memory");
             if (lane == 0) __hip_atomic_store(&s_hflag, (int)tag, __ATOMIC_RELEASE,
                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+            STACK_TRACE(l, 4);
             lds_barrier();  // h staged (compute wavefronts)
+            STACK_TRACE(l, 5);
         }
         barrier_exit(a.bar, a.grp, kStkLead);
     }
@@ -1326,6 +1356,28 @@ int launch_decode_stack(const lily_moe_dims& d, int n_layers, const lily_moe_wei
     hipLaunchKernelGGL(moe_decode_stack_kernel, dim3((unsigned)decode_grid()), dim3(kStkThreads),
                        0, stream, a);
     return check_launch("decode_stack");
+}
+
+// Copies the phase trace of the last lily_moe_decode_stack launch (tracing
+// build only): [min(max_wgs, 256)][64][8] ticks.
+int trace_decode_stack(unsigned long long* dst, int max_wgs, hipStream_t stream) {
+#ifdef LILY_TRACE_ITEMS
+    if (!dst || max_wgs < 1)
+        return set_error(LILY_ERR_INVALID_ARG, "trace_decode_stack: dst non-NULL, max_wgs >= 1");
+    const int n = max_wgs < kTraceStackWgs ? max_wgs : kTraceStackWgs;
+    if (hipStreamSynchronize(stream) != hipSuccess ||
+        hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_stack_trace), sizeof(g_stack_trace[0]) * n, 0,
+                            hipMemcpyDeviceToHost) != hipSuccess)
+        return set_error(LILY_ERR_HIP, "trace_decode_stack: copy failed");
+    return n;
+#else
+    (void)dst;
+    (void)max_wgs;
+    (void)stream;
+    return set_error(LILY_ERR_UNSUPPORTED,
+                     "trace_decode_stack: this library was built without the phase trace "
+                     "(liblily_moe_trace.so has it)");
+#endif
 }
 
 }  // namespace lily

@@ -280,7 +280,7 @@ def test_decode_rejects(lib):
 
 
 def test_trace_only_in_the_tracing_build(lib):
-    """The item trace is the tracing build's: the ordinary library reports it
+    """The traces are the tracing build's: the ordinary library reports them
     as unsupported, the tracing build exports the same symbols and rejects a
     NULL destination before any device call."""
     buf = (ctypes.c_ulonglong * 4)()
@@ -294,3 +294,6 @@ def test_trace_only_in_the_tracing_build(lib):
         assert hasattr(tl, n), f"{n} not exported by the tracing build"
     assert tl.lily_trace_ffn_items(None, 1, None) == L.LILY_ERR_INVALID_ARG
     assert tl.lily_trace_ffn_items(buf, 0, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_trace_decode_stack(buf, 1, None) == L.LILY_ERR_UNSUPPORTED
+    assert tl.lily_trace_decode_stack(None, 1, None) == L.LILY_ERR_INVALID_ARG
+    assert tl.lily_trace_decode_stack(buf, 0, None) == L.LILY_ERR_INVALID_ARG

@@ -194,3 +194,46 @@ def test_decode_stack_one_launch(step):
         assert err <= 1.0, f"layer {layer}: normalised error {err}"
         ora_x = oracle.residual_norm(ora_r, out_o, EPS)
     _flush(f"  worst normalised error over {n_layers} layers: {worst:.4f}")
+
+
+def test_decode_stack_trace():
+    """The tracing build's lily_moe_decode_stack writes the same outputs and
+    final residual as the library, bit for bit, and its phase trace runs in
+    order: per workgroup and layer the lead wavefront's points 0-5 do not go
+    back in time, and a layer starts after the previous one's h was gathered."""
+    cfg = S.CONFIGS["decode40"]
+    n_layers = 8
+    dev = torch.device("cuda")
+    _flush(f"decode stack trace: {n_layers} layers")
+    d = L.dims(1, cfg.H, cfg.F, cfg.E, cfg.k, 32)
+    ws_ = [L.weights_from_host(S.layer_weights(cfg, layer), dev) for layer in range(n_layers)]
+    table = L.layer_table(ws_, dev)
+    lgd = torch.from_numpy(np.stack([S.router_logits(cfg, layer, 0)
+                                     for layer in range(n_layers)])).to(dev)
+    x0d = torch.from_numpy(S.activations(cfg, 0).view(np.int16)).to(dev)
+    ws = L.alloc_workspace(d, dev)
+    sched = torch.zeros(L.LILY_SCHED_INTS, dtype=torch.int32, device=dev)
+
+    def run():
+        r = torch.full((cfg.H,), float("nan"), dtype=torch.float32, device=dev)
+        outs = torch.full((n_layers, cfg.H), -1, dtype=torch.int16, device=dev)
+        ids = torch.full((n_layers, cfg.k), -1, dtype=torch.int32, device=dev)
+        wts = torch.zeros((n_layers, cfg.k), dtype=torch.float32, device=dev)
+        L.lily_moe_decode_stack(d, n_layers, table, lgd, x0d, r, outs, ids, wts, sched, ws, EPS)
+        torch.cuda.synchronize()
+        return r.cpu().numpy(), outs.cpu().numpy()
+
+    r_p, outs_p = run()
+    prod = L.load()
+    try:
+        L.load_trace()
+        r_t, outs_t = run()
+        tr = L.lily_trace_decode_stack().astype(np.int64)
+    finally:
+        L._lib = prod
+    assert np.array_equal(outs_t, outs_p), "the tracing build's layer outputs differ"
+    assert np.array_equal(r_t.view(np.uint32), r_p.view(np.uint32)), "its final residual differs"
+    assert not np.any(sched.cpu().numpy()), "barrier counters and error flag must be zero"
+    t = tr[:, :n_layers, :6]
+    assert np.all(np.diff(t, axis=2) >= 0), "a lead point precedes the one before it"
+    assert np.all(t[:, 1:, 0] >= t[:, :-1, 5]), "a layer starts before the previous one ended"
