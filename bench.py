@@ -414,8 +414,8 @@ def main_prefill(args):
     if args.workload == WORKLOAD and not (args.no_extra or args.router or args.route_host
                                           or args.unfused):
         result["extra"] = {
-            "prefill512": run_prefill_rate(S.CONFIGS["prefill512"], 8, 20, 5),
-            "decode40": run_decode(args, 40, 20, 5, "stack", brief=True),
+            "prefill512": run_prefill_rate(S.CONFIGS["prefill512"], 8, 1000, 200),
+            "decode40": run_decode(args, 40, 50, 20, "stack", brief=True),
         }
     print(json.dumps(result), flush=True)
 
