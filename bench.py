@@ -711,8 +711,9 @@ def main_stack(args):
 def main_peaks(args):
     """Achievable peaks of this device: MFMA throughput on random operands
     at 1 and 2 wavefronts per SIMD (with the shader clock from s_memtime
-    against the 100 MHz s_memrealtime), and HBM streaming reads of 4 GiB
-    with plain and LDS-DMA loads (timed with HIP events, median of 5)."""
+    against the 100 MHz s_memrealtime), the int4 -> bf16 weight rebuild rate
+    on the VALU at 1, 2 and 4 wavefronts per SIMD, and HBM streaming reads of
+    4 GiB with plain and LDS-DMA loads (timed with HIP events, median of 5)."""
     import numpy as np
     import torch
 
@@ -746,6 +747,16 @@ def main_peaks(args):
         res["mfma"][f"{waves // 4}_wave_per_simd"] = {
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_ghz": round(ghz, 3),
             "ms": round(ms, 3)}
+    res["dequant"] = {}
+    for waves in (4, 8, 16):  # 1, 2 and 4 wavefronts per SIMD
+        sink = torch.empty(cus * waves * 64, dtype=torch.int32, device=dev)
+        times = torch.zeros((cus * waves, 2), dtype=torch.int64, device=dev)
+        ms = timed(lambda: L.lily_calib_dequant(cus, waves, 4000, sink, times, stream))
+        t = times.cpu().numpy().astype(np.float64)
+        weights = cus * waves * 64 * 4000 * 64.0
+        res["dequant"][f"{waves // 4}_wave_per_simd"] = {
+            "t_weights_per_s": round(weights / (ms * 1e-3) / 1e12, 2),
+            "clock_ghz": round(float(np.median(t[:, 0] / (t[:, 1] * 10.0))), 3), "ms": round(ms, 3)}
     nbytes = 4 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     for grid_mult in (4, 8):

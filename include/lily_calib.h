@@ -3,7 +3,8 @@
  *
  * They measure what one MI355X achieves, so that the MoE kernels can be
  * reported against measured peaks as well as published ones: MFMA throughput
- * on changing operands with the shader clock it runs at, and streaming HBM
+ * on changing operands with the shader clock it runs at, the rate of the
+ * grouped GEMMs' int4 -> bf16 weight rebuild on the VALU, and streaming HBM
  * reads (plain vector loads, and the LDS DMA loads the grouped GEMMs use).
  * They compute nothing of the MoE layer.
  *
@@ -30,6 +31,17 @@ extern "C" {
    Errors: LILY_ERR_INVALID_ARG, LILY_ERR_HIP. */
 int lily_calib_mfma(int32_t grid, int32_t waves_per_cu, int32_t iters, float* sink,
                     unsigned long long* times, void* stream);
+
+/* The grouped GEMMs' rebuild of int4 weights as bf16(scale * q + bias) on
+   the VALU, alone: grid workgroups of waves_per_cu wavefronts (1..16) each
+   run `iters` rounds of 8 independent words per lane (64 weights per lane
+   per round: per word one add, the 19-instruction rebuild of 8 weights and
+   two 3-input sums). sink: uint32 [grid * waves_per_cu * 64] (written,
+   meaningless); times: uint64 [grid * waves_per_cu][2], per wavefront the
+   shader-clock cycles and 100 MHz wall ticks of its loop. Errors:
+   LILY_ERR_INVALID_ARG, LILY_ERR_HIP. */
+int lily_calib_dequant(int32_t grid, int32_t waves_per_cu, int32_t iters, uint32_t* sink,
+                       unsigned long long* times, void* stream);
 
 /* Reads `bytes` (a multiple of 1024) from src (16-byte aligned) with grid
    workgroups of 256 threads, grid-stride, each thread XOR-reducing what it

@@ -33,7 +33,7 @@ EXPORTS = ("lily_moe_max_blocks", "lily_moe_workspace_bytes", "lily_w4_packed_by
            "lily_residual_norm",
            "lily_last_error",
            # include/lily_calib.h
-           "lily_calib_mfma", "lily_calib_read",
+           "lily_calib_mfma", "lily_calib_dequant", "lily_calib_read",
            # include/lily_trace.h
            "lily_trace_ffn_items", "lily_trace_decode_stack")
 LILY_SCHED_INTS = 1632 + 64 * 512 + 1
@@ -151,6 +151,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lily_calib_mfma.restype = ctypes.c_int
     lib.lily_calib_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.lily_calib_dequant.restype = ctypes.c_int
+    lib.lily_calib_dequant.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.lily_calib_read.restype = ctypes.c_int
     lib.lily_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
@@ -424,6 +427,12 @@ def lily_calib_mfma(grid: int, waves_per_cu: int, iters: int, sink, times, strea
     lib = load()
     _check(lib.lily_calib_mfma(grid, waves_per_cu, iters, _ptr(sink), _ptr(times),
                                _stream(stream)), lib)
+
+
+def lily_calib_dequant(grid: int, waves_per_cu: int, iters: int, sink, times, stream=None) -> None:
+    lib = load()
+    _check(lib.lily_calib_dequant(grid, waves_per_cu, iters, _ptr(sink), _ptr(times),
+                                  _stream(stream)), lib)
 
 
 def lily_calib_read(src, nbytes: int, grid: int, dma: bool, sink, stream=None) -> None:

@@ -124,6 +124,51 @@ __global__ void __launch_bounds__(256) calib_read_kernel(const u32x4* __restrict
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
 }
 
+// The grouped GEMMs' weight rebuild (dequant8: 8 int4 weights -> 4 bf16x2
+// words of bf16(scale * q + bias)) alone: every wavefront runs `iters`
+// rounds over 8 independent words per lane. Per word and round: one add that
+// changes the word (so that no round can be hoisted), dequant8, and two
+// 3-input sums that keep all four results live; 8 weights per word. Lane 0
+// records the wavefront's shader-clock cycles and wall ticks over the loop.
+__global__ void __launch_bounds__(1024) calib_dequant_kernel(int iters, uint32_t* sink,
+                                                             unsigned long long* times) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    uint32_t seed = calib_hash(blockIdx.x * 4096u + threadIdx.x + 1u);
+    uint32_t w[8], acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        seed = calib_hash(seed);
+        w[j] = seed;
+        acc[j] = 0;
+    }
+    seed = calib_hash(seed);
+    const float s512 = (1.0f + (seed & 0xFF) * (1.0f / 256)) * 0.01f * 512.0f;
+    const float bias = ((int)((seed >> 8) & 0xFF) - 128) * (1.0f / 16384);
+    __syncthreads();
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            w[j] += 0x13579BDFu;
+            uint32_t o[4];
+            dequant8(w[j], s512, bias, o);
+            acc[j] += o[0] + o[1];
+            acc[j] += o[2] + o[3];
+        }
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x ^= acc[j];
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+    if (lane == 0) {
+        unsigned long long* tt = times + ((size_t)blockIdx.x * (blockDim.x / kWave) + wave) * 2;
+        tt[0] = t1 - t0;
+        tt[1] = r1 - r0;
+    }
+}
+
 }  // namespace lily
 
 using namespace lily;
@@ -140,6 +185,18 @@ int lily_calib_mfma(int32_t grid, int32_t waves_per_cu, int32_t iters, float* si
     hipLaunchKernelGGL(calib_mfma_kernel, dim3(grid), dim3(waves_per_cu * kWave), 0,
                        reinterpret_cast<hipStream_t>(stream), iters, sink, times);
     return check_launch("calib_mfma");
+}
+
+int lily_calib_dequant(int32_t grid, int32_t waves_per_cu, int32_t iters, uint32_t* sink,
+                       unsigned long long* times, void* stream) {
+    if (grid < 1 || waves_per_cu < 1 || waves_per_cu > 16 || iters < 1)
+        return set_error(LILY_ERR_INVALID_ARG,
+                         "calib_dequant: grid %d >= 1, waves %d in 1..16, iters %d >= 1", grid,
+                         waves_per_cu, iters);
+    if (!sink || !times) return set_error(LILY_ERR_INVALID_ARG, "calib_dequant: NULL buffer");
+    hipLaunchKernelGGL(calib_dequant_kernel, dim3(grid), dim3(waves_per_cu * kWave), 0,
+                       reinterpret_cast<hipStream_t>(stream), iters, sink, times);
+    return check_launch("calib_dequant");
 }
 
 int lily_calib_read(const void* src, size_t bytes, int32_t grid, int32_t dma, uint32_t* sink,

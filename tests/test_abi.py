@@ -217,6 +217,10 @@ def test_calib_rejects(lib):
     assert lib.lily_calib_mfma(0, 4, 100, FAKE, FAKE, None) == L.LILY_ERR_INVALID_ARG
     assert lib.lily_calib_mfma(256, 4, 101, FAKE, FAKE, None) == L.LILY_ERR_INVALID_ARG
     assert lib.lily_calib_mfma(256, 4, 100, None, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_dequant(0, 4, 100, FAKE, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_dequant(256, 17, 100, FAKE, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_dequant(256, 4, 0, FAKE, FAKE, None) == L.LILY_ERR_INVALID_ARG
+    assert lib.lily_calib_dequant(256, 4, 100, FAKE, None, None) == L.LILY_ERR_INVALID_ARG
     assert lib.lily_calib_read(FAKE, 1000, 256, 0, FAKE, None) == L.LILY_ERR_INVALID_ARG
     assert lib.lily_calib_read(FAKE + 4, 1024, 256, 1, FAKE, None) == L.LILY_ERR_INVALID_ARG
     assert lib.lily_calib_read(None, 1024, 256, 1, FAKE, None) == L.LILY_ERR_INVALID_ARG
