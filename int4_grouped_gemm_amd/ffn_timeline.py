@@ -81,6 +81,11 @@ def summarise(traces) -> str:
     lines.append("per queue (workgroups w % 8): busy workgroup-us per launch, median workgroup end:")
     for q in range(QUEUES):
         lines.append(f"  queue {q}: {per_q[q, 0] / n:8.0f}  {per_q[q, 1] / n:6.1f} us")
+    waits = [[wt for _, _, _, down, _, _, _, wt in items_of(tr)[1] if down] for tr in traces]
+    tot = np.mean([sum(w) for w in waits])
+    frac = np.mean([np.mean(np.array(w) > 1.0) for w in waits])
+    lines.append(f"down items' wait for their block's gate/up tiles: {tot:.0f} workgroup-us per "
+                 f"launch in all, {100 * frac:.1f}% of the down items waited more than 1 us")
     from collections import Counter
     c = Counter(tail)
     lines.append("items running after the first 10% of workgroups ran dry (per launch): " +
