@@ -243,6 +243,21 @@ def test_forward_zipf2048_all_tokens(tile_m):
     assert np.array_equal(again, got), "forward is not deterministic"
 
 
+@pytest.mark.parametrize("layer", range(1, 8))
+def test_forward_zipf2048_layer_sets(layer):
+    """The other seven Zipf layer weight sets that bench.py cycles, at its
+    tile height (128): routing bit-exact, and sampled tokens (part edges and
+    the ends included) within the tolerance."""
+    cfg = S.CONFIGS["prefill2048_zipf"]
+    rng = np.random.default_rng(2048 + layer)
+    tokens = sorted(set([0, 127, 128, 1023, 1024, 2047] + rng.choice(cfg.T, 122, replace=False).tolist()))
+    _flush(f"forward prefill2048_zipf layer set {layer}, {len(tokens)} sampled tokens")
+    got, acc, _ = _layer_case(cfg, 128, tokens=tokens, layer=layer)
+    err = G.output_error(got, acc)
+    _flush(f"  normalised error {err:.4f}")
+    assert err <= 1.0, f"normalised error {err}"
+
+
 def test_forward_prefill8192_sampled():
     """One T = 8192 layer call (64 route parts): routing bit-exact, and the
     outputs of sampled tokens (part edges included) within the tolerance."""
